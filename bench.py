@@ -1,0 +1,232 @@
+"""Benchmark: striped ring-attention forward on one MI355X.
+
+One step = stripe-permute Q, K, V (original order -> striped device layout)
+-> all N ring rounds (per-round kernels with the LSE merge fused, heaviest
+tiles first) -> unstripe O and LSE. Inputs are resident in HBM before the
+timed region. Prints one JSON line.
+
+value  = useful causal TFLOP/s of the whole step: 4*Dh flops per live causal
+         pair, B*H*S*(S+1)/2 pairs per step (masked pairs inside partial
+         tiles and skipped tiles are not counted).
+roofline = the ring-round attention kernel (the dominant kernel): useful
+         flops of every launch in the timed region / the sum of their
+         durations, from HIP events recorded on the launch stream around
+         each launch, against the bf16 dense MFMA peak.
+cpu_baseline = the CPU oracle (fp64 numpy dense causal attention) on a
+         bounded sample of the same workload (whole sequence, a subset of
+         heads), rank 0 only.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "useful causal attn TFLOP/s + % bf16 MFMA peak; striped vs contiguous max/mean"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="short")
+    ap.add_argument("--layout", default="striped", choices=["striped", "contiguous"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--no-contiguous", action="store_true", help="skip the contiguous-layout comparison run")
+    return ap.parse_args()
+
+
+def imbalance(live):
+    """Per-round max/mean over devices and the aggregate sum(max)/sum(mean)."""
+    import numpy as np
+    live = np.asarray(live, dtype=np.float64)
+    per = [float(r.max() / r.mean()) if r.mean() > 0 else None for r in live]
+    agg = float(live.max(axis=1).sum() / live.mean(axis=1).sum())
+    return per, agg
+
+
+def cpu_baseline(x, seconds):
+    """Time the oracle on whole-sequence heads until ~`seconds` have elapsed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    q, k, v = (x[n].cpu() for n in ("q", "k", "v"))
+    B, S, H, D = q.shape
+    done, t_total = 0, 0.0
+    while done < H and t_total < seconds:
+        sl = slice(done, done + 1)
+        qh, kh, vh = (t[:, :, sl].double().numpy() for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.dense_causal_attention(qh, kh, vh)
+        t_total += time.perf_counter() - t0
+        done += 1
+    flops = 4.0 * D * B * done * S * (S + 1) / 2
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
+            "kind": "oracle", "sample": f"{done} of {H} heads, whole sequence S={S}, fp64 numpy dense causal "
+                                        f"attention, {t_total:.1f} s; host has {cores} cores available"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the N virtual ring devices are simulated as rounds on a single "
+              f"MI355X, and no multi-GPU path is built (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import striped_ring_attention_amd as sra
+    from striped_ring_attention_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sra.load()
+    w = WORKLOADS[args.workload]
+    if w["dtype"] != torch.bfloat16:
+        print("bench.py times the bf16 workloads", file=sys.stderr)
+        sys.exit(2)
+    B, S, H, D, N = w["batch"], w["seq"], w["heads"], w["head_dim"], w["n_dev"]
+    layout = sra.STRIPED if args.layout == "striped" else sra.CONTIGUOUS
+    dev = torch.device("cuda:0")
+    x = make_inputs(args.workload, device=dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    qd, kd, vd = (torch.empty_like(t) for t in (q, k, v))
+    o_dev = torch.empty_like(q)
+    lse_dev = torch.empty((B, S, H), dtype=torch.float32, device=dev)
+    o, lse = torch.empty_like(q), torch.empty_like(lse_dev)
+    ws = torch.empty(max(1, sra.fwd_workspace_bytes(q, N, layout)), dtype=torch.uint8, device=dev)
+    counts = torch.zeros(N * N, dtype=torch.int64, device=dev)
+
+    def step(events=None, perm_events=None, lay=layout, cnt=None):
+        if lay == sra.STRIPED:
+            if perm_events:
+                perm_events[0].record()
+            for src, dst in ((q, qd), (k, kd), (v, vd)):
+                sra.stripe_permute(src, N, out=dst)
+            if perm_events:
+                perm_events[1].record()
+            sra.ring_attn_fwd(qd, kd, vd, N, lay, out=o_dev, lse=lse_dev, workspace=ws, live_counts=cnt,
+                              round_events=events)
+            if perm_events:
+                perm_events[2].record()
+            sra.unstripe(o_dev, N, out=o)
+            sra.unstripe(lse_dev, N, out=lse)
+            if perm_events:
+                perm_events[3].record()
+        else:
+            sra.ring_attn_fwd(q, k, v, N, lay, out=o, lse=lse, workspace=ws, live_counts=cnt, round_events=events)
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()          # create the underlying HIP event before its handle is passed on
+        return evs
+
+    # Warm-up (and one counted pass for the device-side census).
+    step(cnt=counts)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    round_ev = [new_events(2 * N) for _ in range(K)]
+    perm_ev = [new_events(4) for _ in range(K)] if layout == sra.STRIPED else [None] * K
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        step(events=[e.cuda_event for e in round_ev[i]], perm_events=perm_ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / K
+
+    attn_ms = sum(round_ev[i][2 * r].elapsed_time(round_ev[i][2 * r + 1]) for i in range(K) for r in range(N))
+    launch_ms = attn_ms / (K * N)
+    useful_flops = 4.0 * D * B * H * S * (S + 1) / 2
+    value = useful_flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = useful_flops * K / (attn_ms * 1e-3) / 1e12
+    pairs = sra.count_live_pairs(S, N, layout).numpy() * (B * H)
+    per_launch_flops = [4.0 * D * float(pairs[r].sum()) for r in range(N)]
+
+    perm = {}
+    if layout == sra.STRIPED:
+        p_ms = sum(perm_ev[i][0].elapsed_time(perm_ev[i][1]) for i in range(K)) / K
+        u_ms = sum(perm_ev[i][2].elapsed_time(perm_ev[i][3]) for i in range(K)) / K
+        el = q.element_size()
+        p_bytes = 3 * 2 * q.numel() * el
+        u_bytes = 2 * (o.numel() * el + lse.numel() * 4)
+        perm = {"stripe_permute_qkv_ms": p_ms, "stripe_permute_GBps": p_bytes / (p_ms * 1e-3) / 1e9,
+                "unstripe_o_lse_ms": u_ms, "unstripe_GBps": u_bytes / (u_ms * 1e-3) / 1e9,
+                "hbm_peak_GBps": PEAK_HBM_GBS}
+
+    # Imbalance: host census at 128x128 tiles and at the kernel's own tiles; device counters.
+    tq, tk = sra.kernel_tiles(torch.bfloat16, D)
+    imb = {}
+    for lname, lay in (("contiguous", sra.CONTIGUOUS), ("striped", sra.STRIPED)):
+        live128 = sra.count_live_tiles(S, N, lay, 128, 128)[0].numpy()
+        livek = sra.count_live_tiles(S, N, lay, tq, tk)[0].numpy()
+        per, agg = imbalance(live128)
+        perk, aggk = imbalance(livek)
+        pp, pagg = imbalance(sra.count_live_pairs(S, N, lay).numpy())
+        imb[lname] = {"per_round_max_over_mean_128x128": per, "aggregate_128x128": agg,
+                      f"aggregate_{tq}x{tk}_kernel_tiles": aggk, "aggregate_pairs": pagg}
+    dev_counts = counts.view(N, N).cpu().numpy()
+    host_counts = sra.count_live_tiles(S, N, layout, tq, tk)[0].numpy() * (B * H)
+    imb["device_counters_match_host"] = bool(np.array_equal(dev_counts, host_counts))
+    imb["device_per_round_max_over_mean"] = imbalance(dev_counts)[0]
+
+    # Contiguous layout, same work, for the striped-vs-contiguous comparison.
+    cmp = None
+    if layout == sra.STRIPED and not args.no_contiguous:
+        cev = [new_events(2 * N) for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            step(events=[e.cuda_event for e in cev[i]], lay=sra.CONTIGUOUS)
+        torch.cuda.synchronize()
+        c_ms = sum(cev[i][2 * r].elapsed_time(cev[i][2 * r + 1]) for i in range(K) for r in range(N)) / K
+        c_round = [sum(cev[i][2 * r].elapsed_time(cev[i][2 * r + 1]) for i in range(K)) / K for r in range(N)]
+        s_round = [sum(round_ev[i][2 * r].elapsed_time(round_ev[i][2 * r + 1]) for i in range(K)) / K
+                   for r in range(N)]
+        cmp = {"contiguous_ring_ms": c_ms, "striped_ring_ms": attn_ms / K,
+               "contiguous_useful_TFLOPs": useful_flops / (c_ms * 1e-3) / 1e12,
+               "striped_over_contiguous_speedup": c_ms / (attn_ms / K),
+               "striped_round_ms": s_round, "contiguous_round_ms": c_round}
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "seq_len": S, "heads": H, "head_dim": D,
+                   "ring_devices": N, "layout": args.layout, "causal": True, "pass": "forward"},
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "round_fwd_bf16_d128", "avg_launch_ms": launch_ms,
+                     "flops_per_launch": per_launch_flops},
+        "imbalance": imb, "permutation": perm, "striped_vs_contiguous": cmp,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

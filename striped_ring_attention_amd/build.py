@@ -1,0 +1,75 @@
+"""Build libsra.so (HIP kernels + C ABI) for gfx950 with hipcc.
+
+Usage: python -m striped_ring_attention_amd.build [--jobs N]
+
+Objects go to ``_build/`` at the repository root; the shared library is
+written next to this file so the binding finds it in-tree.
+"""
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libsra.so")
+
+SOURCES = ["sra_api.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip"]
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+COMMON = [
+    "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # No packed-fp32 VALU instructions in device code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src, extra):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line only.
+    err = "\n".join(l for l in p.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{err}")
+    return obj, err
+
+
+def build(jobs=None, extra=(), verbose=False):
+    """Compile every source and link libsra.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
+    objs = []
+    for obj, err in results:
+        objs.append(obj)
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{p.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--extra", nargs="*", default=[], help="extra hipcc flags")
+    args = ap.parse_args()
+    print(build(args.jobs, args.extra, args.verbose))
+
+
+if __name__ == "__main__":
+    main()

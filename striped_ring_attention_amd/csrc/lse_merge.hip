@@ -1,0 +1,78 @@
+// Log-sum-exp merge of per-round partial attention results (fp32).
+//
+// Ring attention is exact (abstract of the Striped Attention paper,
+// pith.science/paper/2311.09431): each round's partial result is softmax
+// attention over that round's keys, and partial results over disjoint key
+// sets combine exactly through their log-sum-exps:
+//   M = max(l_a, l_b), l = M + log(e^(l_a-M) + e^(l_b-M)),
+//   O = e^(l_a-l) O_a + e^(l_b-l) O_b.
+// -inf is the identity (a row with no live key in a round); two -inf give
+// O = 0, l = -inf. HBM-bound: per row it reads O_acc, O_part (Dh fp32 each)
+// and two LSEs, and writes O_acc and one LSE.
+#include "sra_internal.h"
+
+namespace sra {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void merge_weights(float la, float lb, float& wa, float& wb, float& l) {
+    float M = fmaxf(la, lb);
+    if (M == -INFINITY) { wa = 0.f; wb = 0.f; l = -INFINITY; return; }
+    float ea = __expf(la - M);   // exactly 1 for the larger side, 0 for a -inf side
+    float eb = __expf(lb - M);
+    float tot = ea + eb;
+    l = M + __logf(tot);
+    float inv = 1.0f / tot;
+    wa = ea * inv;
+    wb = eb * inv;
+}
+
+// One thread per 4 consecutive values of a row; the Dh/4 threads of one row
+// sit in one wavefront (Dh <= 256), so every lane reads lse_acc[row] before
+// the row's first lane overwrites it.
+__global__ void __launch_bounds__(256) lse_merge_kernel(f32x4* __restrict__ o_acc, float* __restrict__ lse_acc,
+                                                        const f32x4* __restrict__ o_part,
+                                                        const float* __restrict__ lse_part, uint64_t rows,
+                                                        uint32_t q_per_row, int q_shift) {
+    uint64_t total = rows * q_per_row;
+    uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+        uint64_t row = c >> q_shift;
+        uint32_t part = (uint32_t)(c & (q_per_row - 1));
+        float la = lse_acc[row], lb = lse_part[row];
+        float wa, wb, l;
+        merge_weights(la, lb, wa, wb, l);
+        f32x4 a = o_acc[c], b = o_part[c];
+        f32x4 r;
+        if (l == -INFINITY) {
+            r = f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            // A side with zero weight contributes exactly nothing, even if its O holds garbage.
+            r = wa * a;
+            if (wb != 0.f) r = (wa != 0.f) ? r + wb * b : wb * b;
+            if (wa == 0.f) r = wb * b;
+        }
+        o_acc[c] = r;
+        if (part == 0) lse_acc[row] = l;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                            int64_t rows, int64_t head_dim, hipStream_t stream) {
+    uint32_t q = (uint32_t)(head_dim / 4);
+    int shift = 0;
+    while ((1u << shift) < q) ++shift;
+    uint64_t total = (uint64_t)rows * q;
+    const int threads = 256;
+    uint64_t blocks = (total + threads - 1) / threads;
+    if (blocks > 256ull * 64) blocks = 256ull * 64;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, (f32x4*)o_acc, lse_acc,
+                       (const f32x4*)o_part, lse_part, (uint64_t)rows, q, shift);
+    return hipGetLastError();
+}
+
+}  // namespace sra

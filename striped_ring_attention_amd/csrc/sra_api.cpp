@@ -1,0 +1,302 @@
+// Host side of the libsra C ABI: argument validation, the ring-round driver
+// and the host-only census functions. Declarations and contracts: sra.h.
+#include "../../include/sra.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sra_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return SRA_OK;
+    return fail(SRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kMaxSeq = (int64_t)1 << 30;
+
+// Shape checks common to every descriptor-based call.
+int check_layout(int64_t seq, int32_t n_dev, int32_t layout) {
+    if (layout != SRA_LAYOUT_CONTIGUOUS && layout != SRA_LAYOUT_STRIPED)
+        return fail(SRA_ERR_INVALID_ARG, "layout %d is neither contiguous (0) nor striped (1)", layout);
+    if (seq < 1 || seq > kMaxSeq) return fail(SRA_ERR_INVALID_ARG, "seq %lld out of range [1, 2^30]", (long long)seq);
+    if (n_dev < 1 || n_dev > seq)
+        return fail(SRA_ERR_INVALID_ARG, "n_dev %d out of range [1, seq=%lld]", n_dev, (long long)seq);
+    if (seq % n_dev != 0)
+        return fail(SRA_ERR_INVALID_ARG, "seq %lld is not a multiple of n_dev %d", (long long)seq, n_dev);
+    return SRA_OK;
+}
+
+int check_desc(const sra_desc* d) {
+    if (d == nullptr) return fail(SRA_ERR_INVALID_ARG, "desc is NULL");
+    int st = check_layout(d->seq, d->n_dev, d->layout);
+    if (st) return st;
+    if (d->batch < 1 || d->heads < 1 || d->head_dim < 1)
+        return fail(SRA_ERR_INVALID_ARG, "batch, heads and head_dim must be >= 1");
+    if (d->dtype != SRA_DTYPE_F32 && d->dtype != SRA_DTYPE_BF16)
+        return fail(SRA_ERR_INVALID_ARG, "dtype %d is neither f32 (0) nor bf16 (1)", d->dtype);
+    if (d->schedule != SRA_SCHEDULE_PER_ROUND && d->schedule != SRA_SCHEDULE_FUSED)
+        return fail(SRA_ERR_INVALID_ARG, "schedule %d unknown", d->schedule);
+    if (!(d->scale >= 0.f) || std::isinf(d->scale))
+        return fail(SRA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 = 1/sqrt(head_dim))");
+    // Element counts must fit comfortably in int64 and the grid in 32 bits.
+    const double elems = (double)d->batch * (double)d->seq * (double)d->heads * (double)d->head_dim;
+    if (elems > 9.0e18 / 8) return fail(SRA_ERR_INVALID_ARG, "tensor too large");
+    const bool ok = (d->dtype == SRA_DTYPE_BF16 && d->head_dim == 128) ||
+                    (d->dtype == SRA_DTYPE_F32 && (d->head_dim == 64 || d->head_dim == 128));
+    if (!ok)
+        return fail(SRA_ERR_UNSUPPORTED, "no kernel for dtype %d with head_dim %lld (supported: bf16/128, f32/64, f32/128)",
+                    d->dtype, (long long)d->head_dim);
+    const int64_t L = d->seq / d->n_dev;
+    const int64_t tq = d->dtype == SRA_DTYPE_BF16 ? sra::kBf16TileQ : sra::kF32TileQ;
+    const double blocks = (double)((L + tq - 1) / tq) * (double)d->heads * (double)d->n_dev * (double)d->batch;
+    if (blocks > 2147483647.0) return fail(SRA_ERR_INVALID_ARG, "problem needs more than 2^31 workgroups per round");
+    return SRA_OK;
+}
+
+float eff_scale(const sra_desc* d) { return d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim)); }
+
+sra::RoundArgs make_args(const sra_desc* d, const void* q, const void* k, const void* v) {
+    sra::RoundArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.B = d->batch;
+    a.S = d->seq;
+    a.H = d->heads;
+    a.L = d->seq / d->n_dev;
+    a.N = d->n_dev;
+    a.layout = d->layout;
+    a.scale = eff_scale(d);
+    a.scale_log2 = (float)((double)a.scale * 1.4426950408889634074);
+    return a;
+}
+
+hipError_t launch_round(const sra_desc* d, const sra::RoundArgs& a, hipStream_t s) {
+    if (d->dtype == SRA_DTYPE_BF16) return sra::launch_round_bf16_d128(a, s);
+    return sra::launch_round_f32(a, d->head_dim, s);
+}
+
+int64_t elem_bytes(const sra_desc* d) { return d->dtype == SRA_DTYPE_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int sra_abi_version(void) { return SRA_ABI_VERSION; }
+
+const char* sra_status_str(int status) {
+    switch (status) {
+        case SRA_OK: return "SRA_OK";
+        case SRA_ERR_INVALID_ARG: return "SRA_ERR_INVALID_ARG";
+        case SRA_ERR_UNSUPPORTED: return "SRA_ERR_UNSUPPORTED";
+        case SRA_ERR_HIP: return "SRA_ERR_HIP";
+        case SRA_ERR_WORKSPACE: return "SRA_ERR_WORKSPACE";
+        default: return "SRA_ERR_UNKNOWN";
+    }
+}
+
+const char* sra_last_error(void) { return g_err; }
+
+int sra_stripe_index(int64_t seq, int32_t n_dev, int32_t layout, int64_t* perm) {
+    int st = check_layout(seq, n_dev, layout);
+    if (st) return st;
+    if (perm == nullptr) return fail(SRA_ERR_INVALID_ARG, "perm is NULL");
+    const int64_t L = seq / n_dev;
+    for (int64_t dv = 0; dv < n_dev; ++dv)
+        for (int64_t j = 0; j < L; ++j) perm[dv * L + j] = layout == SRA_LAYOUT_STRIPED ? j * n_dev + dv : dv * L + j;
+    return SRA_OK;
+}
+
+int sra_count_live_tiles(const sra_desc* desc, int64_t tile_q, int64_t tile_k, int64_t* live, int64_t* full,
+                         int64_t* partial) {
+    if (desc == nullptr) return fail(SRA_ERR_INVALID_ARG, "desc is NULL");
+    int st = check_layout(desc->seq, desc->n_dev, desc->layout);
+    if (st) return st;
+    if (tile_q < 1 || tile_k < 1) return fail(SRA_ERR_INVALID_ARG, "tile sizes must be >= 1");
+    if (live == nullptr) return fail(SRA_ERR_INVALID_ARG, "live is NULL");
+    const int64_t N = desc->n_dev, L = desc->seq / N;
+    const int64_t nk = (L + tile_k - 1) / tile_k;
+    for (int64_t r = 0; r < N; ++r) {
+        for (int64_t dv = 0; dv < N; ++dv) {
+            const int64_t s = ((dv - r) % N + N) % N;
+            const int64_t delta = sra::live_delta(desc->layout, N, L, dv, s);
+            int64_t nl = 0, nf = 0;
+            for (int64_t j0 = 0; j0 < L; j0 += tile_q) {
+                const int64_t j1 = j0 + tile_q < L ? j0 + tile_q : L;
+                const int64_t c_last = sra::live_keys(j1 - 1, delta, L);    // keys live for the last row
+                const int64_t c_first = sra::live_keys(j0, delta, L);       // keys live for every row
+                nl += (c_last + tile_k - 1) / tile_k;
+                nf += c_first == L ? nk : c_first / tile_k;
+            }
+            live[r * N + dv] = nl;
+            if (full) full[r * N + dv] = nf;
+            if (partial) partial[r * N + dv] = nl - nf;
+        }
+    }
+    return SRA_OK;
+}
+
+int sra_count_live_pairs(const sra_desc* desc, int64_t* pairs) {
+    if (desc == nullptr) return fail(SRA_ERR_INVALID_ARG, "desc is NULL");
+    int st = check_layout(desc->seq, desc->n_dev, desc->layout);
+    if (st) return st;
+    if (pairs == nullptr) return fail(SRA_ERR_INVALID_ARG, "pairs is NULL");
+    const int64_t N = desc->n_dev, L = desc->seq / N;
+    for (int64_t r = 0; r < N; ++r)
+        for (int64_t dv = 0; dv < N; ++dv) {
+            const int64_t s = ((dv - r) % N + N) % N;
+            const int64_t delta = sra::live_delta(desc->layout, N, L, dv, s);
+            int64_t n = 0;
+            for (int64_t j = 0; j < L; ++j) n += sra::live_keys(j, delta, L);
+            pairs[r * N + dv] = n;
+        }
+    return SRA_OK;
+}
+
+int sra_kernel_tiles(const sra_desc* desc, int32_t* tile_q, int32_t* tile_k) {
+    int st = check_desc(desc);
+    if (st) return st;
+    if (tile_q == nullptr || tile_k == nullptr) return fail(SRA_ERR_INVALID_ARG, "tile_q/tile_k is NULL");
+    *tile_q = desc->dtype == SRA_DTYPE_BF16 ? sra::kBf16TileQ : sra::kF32TileQ;
+    *tile_k = desc->dtype == SRA_DTYPE_BF16 ? sra::kBf16TileK : sra::kF32TileK;
+    return SRA_OK;
+}
+
+static int permute_common(const void* src, void* dst, int64_t outer, int64_t seq, int64_t row_bytes, int32_t n_dev,
+                          bool inverse, void* stream) {
+    int st = check_layout(seq, n_dev, SRA_LAYOUT_STRIPED);
+    if (st) return st;
+    if (src == nullptr || dst == nullptr) return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
+    if (outer < 1) return fail(SRA_ERR_INVALID_ARG, "outer must be >= 1");
+    if (row_bytes < 4 || row_bytes % 4 != 0) return fail(SRA_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 4");
+    if (((uintptr_t)src & 3u) || ((uintptr_t)dst & 3u)) return fail(SRA_ERR_INVALID_ARG, "tensors must be 4-byte aligned");
+    const double total = (double)outer * (double)seq * (double)row_bytes;
+    if (total > 4.0e18) return fail(SRA_ERR_INVALID_ARG, "tensor too large");
+    const uintptr_t a0 = (uintptr_t)src, a1 = a0 + (uintptr_t)total, b0 = (uintptr_t)dst, b1 = b0 + (uintptr_t)total;
+    if (a0 < b1 && b0 < a1) return fail(SRA_ERR_INVALID_ARG, "input and output overlap (in-place is not supported)");
+    return hip_status(sra::launch_permute(src, dst, outer, seq, row_bytes, n_dev, inverse, (hipStream_t)stream),
+                      inverse ? "unstripe launch" : "stripe_permute launch");
+}
+
+int sra_stripe_permute(const void* x, void* y, int64_t outer, int64_t seq, int64_t row_bytes, int32_t n_dev,
+                       void* stream) {
+    return permute_common(x, y, outer, seq, row_bytes, n_dev, false, stream);
+}
+
+int sra_unstripe(const void* y, void* x, int64_t outer, int64_t seq, int64_t row_bytes, int32_t n_dev, void* stream) {
+    return permute_common(y, x, outer, seq, row_bytes, n_dev, true, stream);
+}
+
+int sra_ring_round_attn(const sra_desc* desc, int32_t round, int32_t device, const void* q, const void* k,
+                        const void* v, float* o_part, float* lse_part, int64_t* live_counts, void* stream) {
+    int st = check_desc(desc);
+    if (st) return st;
+    if (round < 0 || round >= desc->n_dev)
+        return fail(SRA_ERR_INVALID_ARG, "round %d out of range [0, %d)", round, desc->n_dev);
+    if (device < -1 || device >= desc->n_dev)
+        return fail(SRA_ERR_INVALID_ARG, "device %d out of range [-1, %d)", device, desc->n_dev);
+    if (!q || !k || !v || !o_part || !lse_part) return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part))
+        return fail(SRA_ERR_INVALID_ARG, "q, k, v and o_part must be 16-byte aligned");
+    if (((uintptr_t)lse_part & 3u) || ((uintptr_t)live_counts & 7u))
+        return fail(SRA_ERR_INVALID_ARG, "lse_part / live_counts misaligned");
+    sra::RoundArgs a = make_args(desc, q, k, v);
+    a.o_acc = o_part;
+    a.lse_acc = lse_part;
+    a.o_final = nullptr;
+    a.live_counts = live_counts;
+    a.round = round;
+    a.dev_lo = device < 0 ? 0 : device;
+    a.dev_hi = device < 0 ? desc->n_dev : device + 1;
+    a.mode = 0;
+    return hip_status(launch_round(desc, a, (hipStream_t)stream), "ring_round_attn launch");
+}
+
+int sra_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part, int64_t rows,
+                  int64_t head_dim, void* stream) {
+    if (!o_acc || !lse_acc || !o_part || !lse_part) return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
+    if (rows < 0) return fail(SRA_ERR_INVALID_ARG, "rows must be >= 0");
+    const int64_t q = head_dim / 4;
+    if (head_dim < 4 || head_dim > 256 || head_dim % 4 || (q & (q - 1)))
+        return fail(SRA_ERR_INVALID_ARG, "head_dim must be a power of two in [4, 256]");
+    if (!aligned16(o_acc) || !aligned16(o_part)) return fail(SRA_ERR_INVALID_ARG, "o_acc / o_part must be 16-byte aligned");
+    if (((uintptr_t)lse_acc & 3u) || ((uintptr_t)lse_part & 3u)) return fail(SRA_ERR_INVALID_ARG, "LSE misaligned");
+    if ((double)rows * (double)head_dim > 4.0e18) return fail(SRA_ERR_INVALID_ARG, "tensor too large");
+    return hip_status(sra::launch_lse_merge(o_acc, lse_acc, o_part, lse_part, rows, head_dim, (hipStream_t)stream),
+                      "lse_merge launch");
+}
+
+size_t sra_fwd_workspace_bytes(const sra_desc* desc) {
+    if (check_desc(desc)) return 0;
+    if (desc->dtype == SRA_DTYPE_F32 || desc->n_dev == 1) return 0;   // fp32 accumulates in o itself
+    return (size_t)(desc->batch * desc->seq * desc->heads * desc->head_dim) * sizeof(float);
+}
+
+int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int64_t* live_counts, void* const* round_events,
+                      void* stream) {
+    int st = check_desc(desc);
+    if (st) return st;
+    if (!q || !k || !v || !o || !lse) return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(SRA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (((uintptr_t)lse & 3u) || ((uintptr_t)live_counts & 7u))
+        return fail(SRA_ERR_INVALID_ARG, "lse / live_counts misaligned");
+    if (desc->schedule == SRA_SCHEDULE_FUSED)
+        return fail(SRA_ERR_UNSUPPORTED, "the fused all-rounds schedule is not built");
+    const size_t need = sra_fwd_workspace_bytes(desc);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SRA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (need > 0 && !aligned16(workspace)) return fail(SRA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    // Overlap between inputs and outputs would corrupt inputs that later rounds read.
+    const uintptr_t nbytes = (uintptr_t)(desc->batch * desc->seq * desc->heads * desc->head_dim * elem_bytes(desc));
+    const uintptr_t o0 = (uintptr_t)o, o1 = o0 + nbytes;
+    for (const void* in : {q, k, v}) {
+        const uintptr_t i0 = (uintptr_t)in, i1 = i0 + nbytes;
+        if (i0 < o1 && o0 < i1) return fail(SRA_ERR_INVALID_ARG, "o overlaps an input");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    sra::RoundArgs a = make_args(desc, q, k, v);
+    a.live_counts = live_counts;
+    a.dev_lo = 0;
+    a.dev_hi = desc->n_dev;
+    a.lse_acc = lse;
+    const int N = desc->n_dev;
+    const bool bf16 = desc->dtype == SRA_DTYPE_BF16;
+    a.o_acc = bf16 ? (float*)workspace : (float*)o;
+    a.o_final = o;
+    for (int r = 0; r < N; ++r) {
+        a.round = r;
+        if (bf16) a.mode = r == 0 ? (N == 1 ? 3 : 0) : (r == N - 1 ? 2 : 1);
+        else a.mode = r == 0 ? 0 : 1;   // fp32: the accumulator is the output
+        if (round_events) {
+            hipError_t e = hipEventRecord((hipEvent_t)round_events[2 * r], s);
+            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
+        }
+        hipError_t e = launch_round(desc, a, s);
+        if (e != hipSuccess) return hip_status(e, "ring round launch");
+        if (round_events) {
+            e = hipEventRecord((hipEvent_t)round_events[2 * r + 1], s);
+            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
+        }
+    }
+    return SRA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal declarations shared by the libsra sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sra {
+
+// Liveness in local coordinates.
+//
+// Positions: striped pos(dev, i) = i*N + dev; contiguous pos(dev, i) = dev*L + i
+// (device dev's i-th token; "Summary" ¶1-2 of the Striped Attention summary
+// page). Key k of source device s is live for query j of device d iff
+// pos(s, k) <= pos(d, j). Both layouts reduce this to a shifted causal mask
+//     k < j + delta,   delta = delta(layout, d, s),
+// because pos is affine in the local index with the same slope on both sides:
+//   striped:    k*N + s <= j*N + d  <=>  k <= j + (d - s)/N, and |d - s| < N,
+//               so delta = 1 if s <= d, else 0 (strict diagonal);
+//   contiguous: s*L + k <= d*L + j  <=>  k <= j + (d - s)*L,
+//               so delta = 1 + (d - s)*L (all keys if s < d, none if s > d).
+// The number of live keys of query row j is clamp(j + delta, 0, L), which is
+// nondecreasing in j; a key tile [k0, k1) is therefore FULL for query rows
+// [j0, j1) iff k1 <= clamp(j0 + delta, 0, L) and EMPTY iff
+// k0 >= clamp(j1 - 1 + delta, 0, L).
+__host__ __device__ inline int64_t live_delta(int layout, int64_t n_dev, int64_t L, int64_t d, int64_t s) {
+    if (layout == 1) return s <= d ? 1 : 0;
+    return 1 + (d - s) * L;
+}
+
+__host__ __device__ inline int64_t live_keys(int64_t j, int64_t delta, int64_t L) {
+    int64_t c = j + delta;
+    return c < 0 ? 0 : (c > L ? L : c);
+}
+
+// Launchers (each returns hipSuccess or the launch error). All tensors are in
+// device layout [B, S, H, Dh]; see sra.h for argument meaning.
+struct RoundArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    float* o_acc;        // fp32 [B,S,H,Dh]: partial output, or merge accumulator
+    float* lse_acc;      // fp32 [B,S,H]
+    void* o_final;       // output in the input dtype (last round of the driver), or null
+    int64_t* live_counts;
+    int64_t B, S, H, L;
+    int32_t N, layout, round, dev_lo, dev_hi;   // query devices [dev_lo, dev_hi)
+    float scale;         // softmax scale
+    float scale_log2;    // softmax scale * log2(e)
+    int32_t mode;        // 0: write the partial to (o_acc, lse_acc); 1: merge it into them;
+                         // 2: merge and write the output to o_final (dtype) and lse_acc;
+                         // 3: write the partial as the output (o_final, lse_acc)
+};
+
+hipError_t launch_round_bf16_d128(const RoundArgs& a, hipStream_t stream);
+hipError_t launch_round_f32(const RoundArgs& a, int64_t head_dim, hipStream_t stream);
+
+hipError_t launch_permute(const void* x, void* y, int64_t outer, int64_t seq, int64_t row_bytes,
+                          int32_t n_dev, bool inverse, hipStream_t stream);
+
+hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                            int64_t rows, int64_t head_dim, hipStream_t stream);
+
+constexpr int kBf16TileQ = 128;
+constexpr int kBf16TileK = 64;
+constexpr int kF32TileQ = 64;
+constexpr int kF32TileK = 16;
+
+}  // namespace sra
