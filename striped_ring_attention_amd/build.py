@@ -31,9 +31,15 @@ COMMON = [
 ]
 
 
+# Per-source flags. The attention kernels run with the IEEE mode bit off
+# (no NaN quieting around min/max; infinities still behave) so the row max
+# compiles to bare v_max3_f32.
+PER_SOURCE = {"attn_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_SOURCE.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line only.
     err = "\n".join(l for l in p.stderr.splitlines() if "packed-fp32-ops" not in l)

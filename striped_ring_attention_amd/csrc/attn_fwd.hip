@@ -53,10 +53,18 @@ constexpr int kFlagFinal = 2;   // write the (merged) output to o_final in the i
 constexpr float kLn2 = 0.693147180559945309f;
 
 
-__device__ __forceinline__ float swap_halves(float x) {
-    // Exchange a value between lane l and lane l ^ 32.
+// Reductions across the two 32-lane halves of a wavefront (lane l and l ^ 32).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; with x in both, each lane receives {own, partner}
+// in its two results (in an order that depends on the half), so a symmetric
+// combination of the two is the two-lane reduction in every lane.
+__device__ __forceinline__ float halves_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Log-sum-exp merge weights (natural-log LSEs).
@@ -71,6 +79,15 @@ __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, flo
     wa = ea * inv;
     wb = eb * inv;
 }
+
+// A value the compiler cannot prove wave-uniform (it went through vector
+// registers) but that is: move it to scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) { return (int64_t)uniform_u64((uint64_t)x); }
 
 struct Decoded {
     int64_t b, h, d, s, qt, delta;
@@ -89,6 +106,14 @@ __device__ __forceinline__ Decoded decode_block(const RoundArgs& a, int64_t nqt)
     o.qt = nqt - 1 - qi;
     o.s = (o.d - a.round + a.N) % a.N;
     o.delta = live_delta(a.layout, a.N, a.L, o.d, o.s);
+    // The 64-bit divisions above are expanded on the vector ALU; the results
+    // are per-workgroup constants, so move them back to scalar registers.
+    o.b = uniform_i64(o.b);
+    o.h = uniform_i64(o.h);
+    o.d = uniform_i64(o.d);
+    o.s = uniform_i64(o.s);
+    o.qt = uniform_i64(o.qt);
+    o.delta = uniform_i64(o.delta);
     return o;
 }
 
@@ -109,208 +134,226 @@ struct __align__(16) SmemBf16 {
     bf16 vt[2][D * VP];
 };
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// Low (high) 16-bit halves of a and b packed as {a, b}: one v_perm_b32 each.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Buffer resource over (what is left of) one device's K or V slab of one
+// head: loads at offsets past `bytes` read as zero, so tile loads need
+// neither clamping nor branches.
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
+}
+
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
 
 __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int flags) {
     __shared__ SmemBf16 sm;
 
-    const int64_t L = a.L, S = a.S, H = a.H;
-    const int64_t nqt = (L + BM - 1) / BM;
+    const int64_t nqt = (a.L + BM - 1) / BM;
     const Decoded blk = decode_block(a, nqt);
+    const int L = (int)a.L;   // the host bounds L * H * D so that in-slab offsets fit in 32 bits
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
 
-    const int64_t j0 = blk.qt * BM;
-    const int64_t j1 = (j0 + BM < L) ? j0 + BM : L;
-    const int64_t k_end = live_keys(j1 - 1, blk.delta, L);
-    const int n_tiles = (int)((k_end + BN - 1) / BN);
+    const int j0 = (int)blk.qt * BM;
+    const int j1 = min(j0 + BM, L);
+    const int k_end = (int)live_keys(j1 - 1, blk.delta, L);
+    const int n_tiles = (k_end + BN - 1) / BN;
 
     if (a.live_counts != nullptr && tid == 0 && n_tiles > 0)
         atomicAdd((unsigned long long*)&a.live_counts[(int64_t)a.round * a.N + blk.d], (unsigned long long)n_tiles);
 
     if (n_tiles == 0 && (flags & kFlagMerge) && !(flags & kFlagFinal)) return;   // merging nothing
 
-    const bf16* __restrict__ q = (const bf16*)a.q;
-    const bf16* __restrict__ kg = (const bf16*)a.k;
-    const bf16* __restrict__ vg = (const bf16*)a.v;
-    const int64_t row_stride = H * D;   // elements between consecutive slots
-    const int64_t q_base = ((blk.b * S + blk.d * L) * H + blk.h) * D;
-    const int64_t kv_base = ((blk.b * S + blk.s * L) * H + blk.h) * D;
+    const int rs = (int)(a.H * D);   // elements between consecutive slots
+    const bf16* __restrict__ qp0 = (const bf16*)a.q + ((blk.b * a.S + blk.d * a.L) * a.H + blk.h) * D;
+    const bf16* __restrict__ kp0 = (const bf16*)a.k + ((blk.b * a.S + blk.s * a.L) * a.H + blk.h) * D;
+    const bf16* __restrict__ vp0 = (const bf16*)a.v + ((blk.b * a.S + blk.s * a.L) * a.H + blk.h) * D;
 
-    // This wave's rows and live-key bounds.
-    const int64_t jw0 = j0 + w * 32;
-    const int64_t j = jw0 + c32;
+    // This wave's rows and live-key bounds (live keys of a row form a prefix).
+    const int jw0 = j0 + w * 32;
+    const int j = jw0 + c32;
     const bool row_ok = j < L;
-    const int64_t jw_last = (jw0 + 31 < L) ? jw0 + 31 : L - 1;
-    const int64_t kw_end = (jw0 < L) ? live_keys(jw_last, blk.delta, L) : 0;
-    const int64_t kw_full = (jw0 < L) ? live_keys(jw0, blk.delta, L) : 0;
-    const int64_t c_row = row_ok ? live_keys(j, blk.delta, L) : 0;
+    const int kw_end = jw0 < L ? (int)live_keys(min(jw0 + 31, L - 1), blk.delta, L) : 0;
+    const int kw_full = jw0 < L ? (int)live_keys(jw0, blk.delta, L) : 0;
+    const int c_row = row_ok ? (int)live_keys(j, blk.delta, L) : 0;
 
-    // Q^T operand: lane holds query c32, dims kk*16 + 8*h2 .. +7.
+    // Q^T operand: lane holds query c32, dims kk*16 + 8*h2 .. +7. Rows past
+    // the end read a valid row; they are fully masked and never written.
     bf16x8 qreg[8];
-    if (row_ok) {
-        const bf16x8* qp = (const bf16x8*)(q + q_base + j * row_stride);
+    {
+        const bf16x8* qp = (const bf16x8*)(qp0 + min(j, L - 1) * rs) + h2;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qreg[kk] = qp[2 * kk + h2];
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qreg[kk] = bf16x8{};
+        for (int kk = 0; kk < 8; ++kk) qreg[kk] = qp[2 * kk];
     }
 
     f32x16 oacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;   // running offset (log2 domain), same in both halves
+    float m_run = -INFINITY;   // running offset (log2 domain), equal in both halves
     float l_part = 0.f;        // this half's share of the row sum
     const float sl = a.scale_log2;
 
-    // Global -> register staging of one K/V tile.
-    const int kr = tid >> 2, kc = tid & 3;        // K: key row, 32-dim chunk
-    const int vdp = tid & 63, vkg = tid >> 6;      // V: dim pair, 16-key group
-    bf16x8 kreg[4];
-    uint32_t vreg[16];
+    // Global -> register staging of one K/V tile through buffer loads. Each
+    // tile gets its own buffer resource (base advanced to the tile's first
+    // row, size cut to what is left of the slab, both scalar), so the
+    // per-lane offsets are loop-invariant and rows past the slab end read
+    // as zero (their scores are masked and their V rows get weight 0).
+    //  K: thread -> (key row kr, 32-dim chunk kc), four 16-byte loads.
+    //  V: thread -> (key quad kq, 8-dim chunk dc), one 16-byte load per key
+    //     of the quad; each group of 16 lanes covers all 16 quads of one dim
+    //     chunk, so the transposed LDS writes of a group fill one V^T row.
+    const int kr = tid >> 2, kc = tid & 3;
+    const int kq = tid & 15, dc = tid >> 4;
+    const int row_bytes = rs * 2;
+    const int slab_bytes = __builtin_amdgcn_readfirstlane((L - 1) * row_bytes + D * 2);
+    const int k_voff = kr * row_bytes + kc * 64;
+    const int v_voff = 4 * kq * row_bytes + dc * 16;
+    const uint64_t kbase = uniform_u64((uint64_t)kp0), vbase = uniform_u64((uint64_t)vp0);
+    u32x4 kreg[4], vreg[4];
 
     auto load_tile = [&](int it) {
-        const int64_t k0 = (int64_t)it * BN;
-        const int64_t key = k0 + kr;
-        if (key < L) {
-            const bf16x8* kp = (const bf16x8*)(kg + kv_base + key * row_stride + kc * 32);
+        const int tile_off = it * BN * row_bytes;
+        const int left = slab_bytes - tile_off > 0 ? slab_bytes - tile_off : 0;
+        const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const void*)(kbase + tile_off), left);
+        const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const void*)(vbase + tile_off), left);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kreg[i] = kp[i];
-        } else {
+        for (int i = 0; i < 4; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + 16 * i, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kreg[i] = bf16x8{};
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t vkey = k0 + vkg * 16 + i;
-            vreg[i] = (vkey < L) ? *(const uint32_t*)(vg + kv_base + vkey * row_stride + 2 * vdp) : 0u;
-        }
+        for (int r = 0; r < 4; ++r) vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + r * row_bytes, 0, 0);
     };
+    // V^T column of key quad kq: within each 16-key group the quads are
+    // stored in the order [0, 2, 1, 3] (keys [0-3, 8-11, 4-7, 12-15]).
+    const int vt_col = 16 * (kq >> 2) + 4 * ((kq & 1) * 2 + ((kq >> 1) & 1));
     auto store_tile = [&](int buf) {
         bf16* kd = &sm.k[buf][kr * KP + kc * 32];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(bf16x8*)(kd + 8 * i) = kreg[i];
-        // V^T rows 2*vdp (low halves) and 2*vdp+1 (high halves); within the
-        // 16-key group the order is [0-3, 8-11 | 4-7, 12-15].
-        u32x4 lo_a = {pack_lo(vreg[0], vreg[1]), pack_lo(vreg[2], vreg[3]), pack_lo(vreg[8], vreg[9]), pack_lo(vreg[10], vreg[11])};
-        u32x4 lo_b = {pack_lo(vreg[4], vreg[5]), pack_lo(vreg[6], vreg[7]), pack_lo(vreg[12], vreg[13]), pack_lo(vreg[14], vreg[15])};
-        u32x4 hi_a = {pack_hi(vreg[0], vreg[1]), pack_hi(vreg[2], vreg[3]), pack_hi(vreg[8], vreg[9]), pack_hi(vreg[10], vreg[11])};
-        u32x4 hi_b = {pack_hi(vreg[4], vreg[5]), pack_hi(vreg[6], vreg[7]), pack_hi(vreg[12], vreg[13]), pack_hi(vreg[14], vreg[15])};
-        bf16* v0 = &sm.vt[buf][(2 * vdp) * VP + vkg * 16];
-        bf16* v1 = v0 + VP;
-        *(u32x4*)(v0) = lo_a;
-        *(u32x4*)(v0 + 8) = lo_b;
-        *(u32x4*)(v1) = hi_a;
-        *(u32x4*)(v1 + 8) = hi_b;
+        for (int i = 0; i < 4; ++i) *(u32x4*)(kd + 8 * i) = kreg[i];
+        // vreg[r][p] holds dims (2p, 2p+1) of key 4*kq + r.
+        bf16* vd = &sm.vt[buf][(8 * dc) * VP + vt_col];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            uint2 lo = {pack_lo(vreg[0][p], vreg[1][p]), pack_lo(vreg[2][p], vreg[3][p])};
+            uint2 hi = {pack_hi(vreg[0][p], vreg[1][p]), pack_hi(vreg[2][p], vreg[3][p])};
+            *(uint2*)(vd + (2 * p) * VP) = lo;
+            *(uint2*)(vd + (2 * p + 1) * VP) = hi;
+        }
+    };
+
+    // One step over the tile in LDS buffer `cur` for this wave's 32 rows.
+    // kMasked: the tile is not fully live for every row of the wave.
+    auto step = [&](auto masked_tag, int cur, int k0) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        const bf16* ks = sm.k[cur] + c32 * KP + 8 * h2;
+        f32x16 s0, s1;
+        {
+            bf16x8 kf[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) kf[kk] = *(const bf16x8*)(ks + kk * 16);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+            for (int kk = 1; kk < 8; ++kk) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], s0, 0, 0, 0);
+        }
+        {
+            bf16x8 kf[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) kf[kk] = *(const bf16x8*)(ks + 32 * KP + kk * 16);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+            for (int kk = 1; kk < 8; ++kk) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], s1, 0, 0, 0);
+        }
+        if constexpr (kMasked) {
+            // key offset in the tile of accumulator element i of block kb is
+            // kb*32 + 8*(i/4) + 4*h2 + i%4; live iff key < c_row.
+            const int lim = c_row - k0 - 4 * h2;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int off = 8 * (i >> 2) + (i & 3);
+                if (off >= lim) s0[i] = -INFINITY;
+                if (off + 32 >= lim) s1[i] = -INFINITY;
+            }
+        }
+        // Row max over this tile (raw scores; scale > 0 keeps the order).
+        float mx = fmaxf(fmaxf(s0[0], s1[0]), s0[1]);
+#pragma unroll
+        for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s1[i]), fmaxf(s0[i + 1], s1[i + 1]));
+        mx = fmaxf(fmaxf(mx, s1[15]), s0[15]);
+        mx = halves_max(mx);
+        const float m_tile = mx * sl;
+        const bool need = m_tile > m_run + kTau;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            const float m_new = need ? fmaxf(m_run, m_tile) : m_run;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+            l_part *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        // p = 2^(s*scale*log2e - m), summed in fp32 and rounded to bf16 for P^T.
+        bf16x8 pop[2][2];
+        float lsum0 = 0.f, lsum1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], sl, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], sl, -m_use));
+            lsum0 += p0;
+            lsum1 += p1;
+            pop[0][i >> 3][i & 7] = (bf16)p0;
+            pop[1][i >> 3][i & 7] = (bf16)p1;
+        }
+        l_part += lsum0 + lsum1;
+        const bf16* vts = sm.vt[cur] + c32 * VP + 8 * h2;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int kk2 = 0; kk2 < 2; ++kk2) {
+                bf16x8 vf[4];
+#pragma unroll
+                for (int db = 0; db < 4; ++db) vf[db] = *(const bf16x8*)(vts + db * 32 * VP + kb * 32 + kk2 * 16);
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pop[kb][kk2], oacc[db], 0, 0, 0);
+            }
+        }
     };
 
     if (n_tiles > 0) {
         load_tile(0);
         store_tile(0);
-        __syncthreads();
     }
+    // Every global load issued so far (Q and tile 0) has landed before the
+    // loop, so waits inside the loop only ever cover the prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
     for (int it = 0; it < n_tiles; ++it) {
         const int cur = it & 1;
-        const bool has_next = it + 1 < n_tiles;
-        if (has_next) load_tile(it + 1);
-
-        const int64_t k0 = (int64_t)it * BN;
-        // Live 32-key blocks of this tile for this wave (0, 1 or 2); wave-uniform.
-        const int64_t rem = kw_end - k0;
-        const int n_kb = rem <= 0 ? 0 : (rem > 32 ? 2 : 1);
-        if (n_kb > 0) {
-            const bf16* ks = sm.k[cur];
-            const bf16* vts = sm.vt[cur];
-            f32x16 sacc[2];
-            sacc[0] = f32x16{};
-            sacc[1] = f32x16{};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb < n_kb) {
-#pragma unroll
-                    for (int kk = 0; kk < 8; ++kk) {
-                        bf16x8 kop = *(const bf16x8*)(ks + (kb * 32 + c32) * KP + kk * 16 + 8 * h2);
-                        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], sacc[kb], 0, 0, 0);
-                    }
-                }
-            }
-            // Mask: only when the tile is not fully live for every row of the wave.
-            if (k0 + BN > kw_full) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    if (kb < n_kb) {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int64_t key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-                            if (key >= c_row) sacc[kb][i] = -INFINITY;
-                        }
-                    }
-                }
-            }
-            // Row max over this tile (raw scores; scale > 0 keeps the order).
-            float mx = sacc[0][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[0][i]);
-            if (n_kb > 1) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[1][i]);
-            }
-            mx = fmaxf(mx, swap_halves(mx));
-            const float m_tile = mx * sl;
-            const bool need = m_tile > m_run + kTau;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                const float m_new = need ? fmaxf(m_run, m_tile) : m_run;
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-#pragma unroll
-                for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-                l_part *= alpha;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-            // p = 2^(s*scale*log2e - m); P^T operands for the PV product.
-            bf16x8 pop[2][2];
-            float lsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb < n_kb) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], sl, -m_use));
-                        lsum += p;
-                        pop[kb][i >> 3][i & 7] = (bf16)p;
-                    }
-                }
-            }
-            l_part += lsum;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb < n_kb) {
-#pragma unroll
-                    for (int kk2 = 0; kk2 < 2; ++kk2) {
-#pragma unroll
-                        for (int db = 0; db < 4; ++db) {
-                            bf16x8 vop = *(const bf16x8*)(vts + (db * 32 + c32) * VP + kb * 32 + kk2 * 16 + 8 * h2);
-                            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[kb][kk2], oacc[db], 0, 0, 0);
-                        }
-                    }
-                }
-            }
+        // Prefetch the next tile (past the last tile the loads read zeros
+        // into the idle buffer; no branch needed).
+        load_tile(it + 1);
+        const int k0 = it * BN;
+        if (k0 < kw_end) {
+            if (k0 + BN <= kw_full) step(BoolTag<false>{}, cur, k0);
+            else step(BoolTag<true>{}, cur, k0);
         }
-
-        if (has_next) store_tile(cur ^ 1);
+        store_tile(cur ^ 1);
         __syncthreads();
     }
 
     // Finish the row: l = both halves' sums; O = O / l; lse in natural log.
-    const float l_tot = l_part + swap_halves(l_part);
+    const float l_tot = halves_sum(l_part);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float lse_b = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     if (!row_ok) return;
 
-    const int64_t row = (blk.b * S + blk.d * L + j) * H + blk.h;   // (b, slot, h) row index
+    const int64_t row = (blk.b * a.S + blk.d * a.L + j) * a.H + blk.h;   // (b, slot, h) row index
     float wa = 0.f, wb = 1.f, l_out = lse_b;
     if (flags & kFlagMerge) {
         const float la = a.lse_acc[row];
