@@ -96,7 +96,15 @@ struct Decoded {
 __device__ __forceinline__ Decoded decode_block(const RoundArgs& a, int64_t nqt) {
     // Block order: query tiles fastest and heaviest first (the last query
     // tile of a device has the most live keys), then heads, devices, batch.
+    // Workgroups are dealt to the 8 XCDs round-robin (block i on XCD i mod 8)
+    // and each XCD has its own L2, so hardware block i is remapped to logical
+    // block (i mod 8) * (n / 8) + i / 8: every XCD gets a contiguous range of
+    // logical blocks, and the query tiles that stream the same K/V slab run
+    // on the same XCD and share its L2.
+    const int64_t n = (int64_t)gridDim.x;
+    const int64_t n8 = n & ~(int64_t)7;
     int64_t bid = blockIdx.x;
+    if (bid < n8) bid = (bid & 7) * (n8 >> 3) + (bid >> 3);
     Decoded o;
     int64_t qi = bid % nqt; bid /= nqt;
     o.h = bid % a.H; bid /= a.H;
@@ -120,18 +128,18 @@ __device__ __forceinline__ Decoded decode_block(const RoundArgs& a, int64_t nqt)
 // ---------------------------------------------------------------- bf16 ----
 
 constexpr int D = 128;
-constexpr int BM = kBf16TileQ;   // 128 query rows per workgroup
-constexpr int BN = kBf16TileK;   // 64 keys per step
-constexpr int NT = 256;          // 4 wavefronts
+constexpr int BM = kBf16TileQ;   // 256 query rows per workgroup: 8 wavefronts x 32
+constexpr int BN = kBf16TileK;   // 64 keys per tile
+constexpr int NT = 512;          // 8 wavefronts in two groups of 4: one wave of each group per SIMD
 constexpr int KP = D + 8;        // K tile row pitch in LDS (elements)
 constexpr int VP = BN + 8;       // V^T tile row pitch in LDS (elements)
 constexpr float kTau = 8.0f;     // lazy-rescale threshold (log2 units)
 
-static_assert(BM == 128 && BN == 64 && NT == 256, "thread mappings below assume these");
+static_assert(BM == 256 && BN == 64 && NT == 512, "thread mappings below assume these");
 
 struct __align__(16) SmemBf16 {
-    bf16 k[2][BN * KP];
-    bf16 vt[2][D * VP];
+    bf16 k[2][BN * KP];    // key tiles, row-major
+    bf16 vt[2][D * VP];    // value tiles, dimension-major (transposed)
 };
 
 // Low (high) 16-bit halves of a and b packed as {a, b}: one v_perm_b32 each.
@@ -142,17 +150,62 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __b
 // head: loads at offsets past `bytes` read as zero, so tile loads need
 // neither clamping nor branches.
 constexpr int kBufferFlags = 0x00020000;
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
 }
 
-template <bool B>
-struct BoolTag {
-    static constexpr bool value = B;
+// Walks the (round, key tile) pairs one workgroup visits, in ring order:
+// rounds r_lo .. r_hi-1, and within a round the key tiles of the source
+// device that hold at least one live key for the workgroup's last query row.
+// All fields are wave-uniform.
+struct TileCursor {
+    int r, kt, nt;        // round, key tile within the round, tiles in the round
+    int s, delta;         // source device of the round, live-key shift
 };
 
-__global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int flags) {
+// Live keys of local query row j (int32 form of live_keys; |delta| <= L + 1).
+__device__ __forceinline__ int live32(int j, int delta, int L) { return min(max(j + delta, 0), L); }
+
+struct RoundGeom {
+    int L, N, layout, d, j_last, r_hi;
+    __device__ __forceinline__ void enter(TileCursor& c) const {
+        c.s = __builtin_amdgcn_readfirstlane((d - c.r + N) % N);
+        int64_t dl = live_delta(layout, N, L, d, c.s);
+        dl = dl < -(int64_t)L - 1 ? -(int64_t)L - 1 : (dl > (int64_t)L + 1 ? (int64_t)L + 1 : dl);
+        c.delta = __builtin_amdgcn_readfirstlane((int)dl);
+        c.nt = __builtin_amdgcn_readfirstlane((live32(j_last, c.delta, L) + BN - 1) / BN);
+        c.kt = 0;
+    }
+    // Move to the first tile at or after the cursor's position.
+    __device__ __forceinline__ void settle(TileCursor& c) const {
+        while (c.kt >= c.nt && c.r + 1 < r_hi) {
+            ++c.r;
+            enter(c);
+        }
+    }
+    __device__ __forceinline__ void advance(TileCursor& c) const {
+        ++c.kt;
+        settle(c);
+    }
+};
+
+// kFused = false: one ring round per launch (a.round), with the epilogue
+//   writing, merging or finishing per a.mode.
+// kFused = true: all N rounds in one launch; the online softmax carries the
+//   running (O, max, sum) across rounds, which is the log-sum-exp merge of
+//   the per-round partial results, and the epilogue writes the output.
+//
+// Schedule ("ping-pong"): the two groups of 4 wavefronts run the same tile
+// sequence one phase apart. In phase X(t) a wave issues its MFMAs: O += P V
+// for tile t-1, then S = K Q^T for tile t. In phase Y(t) it runs the softmax
+// of tile t on the vector ALU. Group 1 starts one phase late, so on every
+// SIMD one wave is in X while the other is in Y, and a workgroup barrier
+// separates consecutive phases. Group 1 also stages K/V tiles: in its Y(t)
+// it writes K(t+2) and V(t+1) (loaded two phases earlier) to LDS and issues
+// the global loads of K(t+3) and V(t+2). With K(t) read in X(t) of both
+// groups and V(t) in X(t+1) of both groups, two LDS buffers each suffice.
+template <bool kFused>
+__global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int flags) {
     __shared__ SmemBf16 sm;
 
     const int64_t nqt = (a.L + BM - 1) / BM;
@@ -160,29 +213,42 @@ __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int fl
     const int L = (int)a.L;   // the host bounds L * H * D so that in-slab offsets fit in 32 bits
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
+    const int grp = w >> 2;
+    const int lt = tid & 255;   // loader thread index within group 1
 
     const int j0 = (int)blk.qt * BM;
     const int j1 = min(j0 + BM, L);
-    const int k_end = (int)live_keys(j1 - 1, blk.delta, L);
-    const int n_tiles = (k_end + BN - 1) / BN;
+    const int d = (int)blk.d;
+    const RoundGeom geo{L, a.N, a.layout, d, j1 - 1, kFused ? a.N : a.round + 1};
 
-    if (a.live_counts != nullptr && tid == 0 && n_tiles > 0)
-        atomicAdd((unsigned long long*)&a.live_counts[(int64_t)a.round * a.N + blk.d], (unsigned long long)n_tiles);
-
-    if (n_tiles == 0 && (flags & kFlagMerge) && !(flags & kFlagFinal)) return;   // merging nothing
+    // Tiles per round; device-side live-tile census.
+    int n_tiles = 0;
+    {
+        TileCursor c;
+        for (c.r = kFused ? 0 : a.round; c.r < geo.r_hi; ++c.r) {
+            geo.enter(c);
+            n_tiles += c.nt;
+            if (a.live_counts != nullptr && tid == 0 && c.nt > 0)
+                atomicAdd((unsigned long long*)&a.live_counts[(int64_t)c.r * a.N + d], (unsigned long long)c.nt);
+        }
+    }
+    if (!kFused && n_tiles == 0 && (flags & kFlagMerge) && !(flags & kFlagFinal)) return;   // merging nothing
 
     const int rs = (int)(a.H * D);   // elements between consecutive slots
+    const int row_bytes = rs * 2;
     const bf16* __restrict__ qp0 = (const bf16*)a.q + ((blk.b * a.S + blk.d * a.L) * a.H + blk.h) * D;
-    const bf16* __restrict__ kp0 = (const bf16*)a.k + ((blk.b * a.S + blk.s * a.L) * a.H + blk.h) * D;
-    const bf16* __restrict__ vp0 = (const bf16*)a.v + ((blk.b * a.S + blk.s * a.L) * a.H + blk.h) * D;
+    // Slab of device s for this (b, h) starts at kv_head + s * slab_stride bytes.
+    const uint64_t kv_head_k = uniform_u64((uint64_t)((const bf16*)a.k + (blk.b * a.S * a.H + blk.h) * D));
+    const uint64_t kv_head_v = uniform_u64((uint64_t)((const bf16*)a.v + (blk.b * a.S * a.H + blk.h) * D));
+    const uint64_t slab_stride = (uint64_t)a.L * (uint64_t)row_bytes;
+    const int slab_bytes = __builtin_amdgcn_readfirstlane((L - 1) * row_bytes + D * 2);
 
-    // This wave's rows and live-key bounds (live keys of a row form a prefix).
+    // This wave's 32 rows and live-key bounds (live keys of a row form a prefix).
     const int jw0 = j0 + w * 32;
     const int j = jw0 + c32;
     const bool row_ok = j < L;
-    const int kw_end = jw0 < L ? (int)live_keys(min(jw0 + 31, L - 1), blk.delta, L) : 0;
-    const int kw_full = jw0 < L ? (int)live_keys(jw0, blk.delta, L) : 0;
-    const int c_row = row_ok ? (int)live_keys(j, blk.delta, L) : 0;
+    const bool wave_live = jw0 < L;
+    const int jw_last = min(jw0 + 31, L - 1);
 
     // Q^T operand: lane holds query c32, dims kk*16 + 8*h2 .. +7. Rows past
     // the end read a valid row; they are fully masked and never written.
@@ -191,6 +257,9 @@ __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int fl
         const bf16x8* qp = (const bf16x8*)(qp0 + min(j, L - 1) * rs) + h2;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) qreg[kk] = qp[2 * kk];
+        // Let the Q loads land before any K/V load is issued: later waits on
+        // the K/V prefetch then never hold up the MFMAs that read Q.
+        __builtin_amdgcn_s_waitcnt(0);
     }
 
     f32x16 oacc[4];
@@ -200,41 +269,46 @@ __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int fl
     float l_part = 0.f;        // this half's share of the row sum
     const float sl = a.scale_log2;
 
-    // Global -> register staging of one K/V tile through buffer loads. Each
-    // tile gets its own buffer resource (base advanced to the tile's first
-    // row, size cut to what is left of the slab, both scalar), so the
-    // per-lane offsets are loop-invariant and rows past the slab end read
-    // as zero (their scores are masked and their V rows get weight 0).
+    // K/V staging by group 1 through buffer loads. Each tile gets its own
+    // buffer resource (base advanced to the tile's first row, size cut to what
+    // is left of the slab, both scalar), so the per-lane offsets are
+    // loop-invariant and rows past the slab end read as zero (their scores
+    // are masked and their V rows get weight 0).
     //  K: thread -> (key row kr, 32-dim chunk kc), four 16-byte loads.
     //  V: thread -> (key quad kq, 8-dim chunk dc), one 16-byte load per key
     //     of the quad; each group of 16 lanes covers all 16 quads of one dim
     //     chunk, so the transposed LDS writes of a group fill one V^T row.
-    const int kr = tid >> 2, kc = tid & 3;
-    const int kq = tid & 15, dc = tid >> 4;
-    const int row_bytes = rs * 2;
-    const int slab_bytes = __builtin_amdgcn_readfirstlane((L - 1) * row_bytes + D * 2);
+    const int kr = lt >> 2, kc = lt & 3;
+    const int kq = lt & 15, dc = lt >> 4;
     const int k_voff = kr * row_bytes + kc * 64;
     const int v_voff = 4 * kq * row_bytes + dc * 16;
-    const uint64_t kbase = uniform_u64((uint64_t)kp0), vbase = uniform_u64((uint64_t)vp0);
     u32x4 kreg[4], vreg[4];
 
-    auto load_tile = [&](int it) {
-        const int tile_off = it * BN * row_bytes;
-        const int left = slab_bytes - tile_off > 0 ? slab_bytes - tile_off : 0;
-        const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const void*)(kbase + tile_off), left);
-        const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const void*)(vbase + tile_off), left);
+    auto tile_rsrc = [&](uint64_t head, const TileCursor& c, bool valid) {
+        const int tile_off = c.kt * BN * row_bytes;
+        int left = slab_bytes - tile_off;
+        left = (valid && left > 0) ? left : 0;
+        return slab_rsrc((const void*)(head + (uint64_t)c.s * slab_stride + (uint64_t)tile_off), left);
+    };
+    auto load_k = [&](const TileCursor& c, bool valid) {
+        const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(kv_head_k, c, valid);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + 16 * i, 0, 0);
+        for (int i = 0; i < 4; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, k_voff + 16 * i, 0, 0);
+    };
+    auto load_v = [&](const TileCursor& c, bool valid) {
+        const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(kv_head_v, c, valid);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + r * row_bytes, 0, 0);
+        for (int r = 0; r < 4; ++r) vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, v_voff + r * row_bytes, 0, 0);
+    };
+    auto store_k = [&](int buf) {
+        bf16* kd = &sm.k[buf][kr * KP + kc * 32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4*)(kd + 8 * i) = kreg[i];
     };
     // V^T column of key quad kq: within each 16-key group the quads are
     // stored in the order [0, 2, 1, 3] (keys [0-3, 8-11, 4-7, 12-15]).
     const int vt_col = 16 * (kq >> 2) + 4 * ((kq & 1) * 2 + ((kq >> 1) & 1));
-    auto store_tile = [&](int buf) {
-        bf16* kd = &sm.k[buf][kr * KP + kc * 32];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(kd + 8 * i) = kreg[i];
+    auto store_v = [&](int buf) {
         // vreg[r][p] holds dims (2p, 2p+1) of key 4*kq + r.
         bf16* vd = &sm.vt[buf][(8 * dc) * VP + vt_col];
 #pragma unroll
@@ -246,70 +320,31 @@ __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int fl
         }
     };
 
-    // One step over the tile in LDS buffer `cur` for this wave's 32 rows.
-    // kMasked: the tile is not fully live for every row of the wave.
-    auto step = [&](auto masked_tag, int cur, int k0) {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-        const bf16* ks = sm.k[cur] + c32 * KP + 8 * h2;
-        f32x16 s0, s1;
-        {
-            bf16x8 kf[8];
+    // S^T = K Q^T over the K tile in buffer `buf`: sacc[kb] holds keys
+    // kb*32 .. kb*32+31 of the tile against this wave's 32 queries.
+    f32x16 sacc[2];
+    auto compute_s = [&](int buf) {
+        const bf16* ks = sm.k[buf] + c32 * KP + 8 * h2;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) kf[kk] = *(const bf16x8*)(ks + kk * 16);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-            for (int kk = 1; kk < 8; ++kk) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], s0, 0, 0, 0);
+        for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 k0f = *(const bf16x8*)(ks + kk * 16);
+            const bf16x8 k1f = *(const bf16x8*)(ks + 32 * KP + kk * 16);
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qreg[kk], kk == 0 ? f32x16{} : sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qreg[kk], kk == 0 ? f32x16{} : sacc[1], 0, 0, 0);
         }
-        {
-            bf16x8 kf[8];
+    };
+
+    // O^T += V^T P^T over the V tile in buffer `buf`, after applying the
+    // pending rescale of O (rare: only when the running offset was raised).
+    bf16x8 pop[2][2];
+    bool resc = false;
+    float alpha_p = 1.f;
+    auto compute_pv = [&](int buf) {
+        if (resc) {
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) kf[kk] = *(const bf16x8*)(ks + 32 * KP + kk * 16);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qreg[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-            for (int kk = 1; kk < 8; ++kk) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[kk], s1, 0, 0, 0);
+            for (int db = 0; db < 4; ++db) oacc[db] *= alpha_p;
         }
-        if constexpr (kMasked) {
-            // key offset in the tile of accumulator element i of block kb is
-            // kb*32 + 8*(i/4) + 4*h2 + i%4; live iff key < c_row.
-            const int lim = c_row - k0 - 4 * h2;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int off = 8 * (i >> 2) + (i & 3);
-                if (off >= lim) s0[i] = -INFINITY;
-                if (off + 32 >= lim) s1[i] = -INFINITY;
-            }
-        }
-        // Row max over this tile (raw scores; scale > 0 keeps the order).
-        float mx = fmaxf(fmaxf(s0[0], s1[0]), s0[1]);
-#pragma unroll
-        for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s1[i]), fmaxf(s0[i + 1], s1[i + 1]));
-        mx = fmaxf(fmaxf(mx, s1[15]), s0[15]);
-        mx = halves_max(mx);
-        const float m_tile = mx * sl;
-        const bool need = m_tile > m_run + kTau;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-            const float m_new = need ? fmaxf(m_run, m_tile) : m_run;
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-            l_part *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        // p = 2^(s*scale*log2e - m), summed in fp32 and rounded to bf16 for P^T.
-        bf16x8 pop[2][2];
-        float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], sl, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], sl, -m_use));
-            lsum0 += p0;
-            lsum1 += p1;
-            pop[0][i >> 3][i & 7] = (bf16)p0;
-            pop[1][i >> 3][i & 7] = (bf16)p1;
-        }
-        l_part += lsum0 + lsum1;
-        const bf16* vts = sm.vt[cur] + c32 * VP + 8 * h2;
+        const bf16* vts = sm.vt[buf] + c32 * VP + 8 * h2;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -324,28 +359,105 @@ __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int fl
         }
     };
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
+    // Softmax of the tile at cursor c: mask (only if not fully live for the
+    // wave's first row), row max, lazy rescale, p = 2^(s*scale*log2e - m),
+    // fp32 row sum, bf16 P^T operands.
+    auto softmax = [&](const TileCursor& c) {
+        const int k0 = c.kt * BN;
+        if (k0 + BN > live32(jw0, c.delta, L)) {
+            const int lim = (row_ok ? live32(j, c.delta, L) : 0) - k0 - 4 * h2;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int off = 8 * (i >> 2) + (i & 3);
+                if (off >= lim) sacc[0][i] = -INFINITY;
+                if (off + 32 >= lim) sacc[1][i] = -INFINITY;
+            }
+        }
+        float mx = fmaxf(fmaxf(sacc[0][0], sacc[1][0]), sacc[0][1]);
+#pragma unroll
+        for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[1][i]), fmaxf(sacc[0][i + 1], sacc[1][i + 1]));
+        mx = fmaxf(fmaxf(mx, sacc[1][15]), sacc[0][15]);
+        const float m_tile = halves_max(mx) * sl;   // raw max times scale (> 0 keeps the order)
+        const bool need = m_tile > m_run + kTau;
+        // The O rescale this implies is applied in the next MFMA phase, just
+        // before this tile's P V is accumulated (keeps O's registers in place).
+        resc = __builtin_amdgcn_ballot_w64(need) != 0;
+        {
+            const float m_new = need ? fmaxf(m_run, m_tile) : m_run;
+            alpha_p = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_part *= alpha_p;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], sl, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], sl, -m_use));
+            ls0 += p0;
+            ls1 += p1;
+            pop[0][i >> 3][i & 7] = (bf16)p0;
+            pop[1][i >> 3][i & 7] = (bf16)p1;
+        }
+        l_part += ls0 + ls1;
+    };
+
+    // Does this wave have a live key in the tile at cursor c?
+    auto wave_active = [&](const TileCursor& c) {
+        return wave_live && c.kt * BN < live32(jw_last, c.delta, L);
+    };
+
+    TileCursor c0;
+    c0.r = kFused ? 0 : a.round;
+    geo.enter(c0);
+    geo.settle(c0);
+    TileCursor c1 = c0;
+    geo.advance(c1);
+    TileCursor c2 = c1;
+    geo.advance(c2);
+    TileCursor c3 = c2;
+    geo.advance(c3);
+
+    // Prologue (group 1): K(0), V(0) and K(1) into LDS; K(2), V(1) in flight.
+    if (grp == 1) {
+        load_k(c0, n_tiles > 0);
+        load_v(c0, n_tiles > 0);
+        store_k(0);
+        store_v(0);
+        load_k(c1, n_tiles > 1);
+        store_k(1);
+        load_k(c2, n_tiles > 2);
+        load_v(c1, n_tiles > 1);
     }
-    // Every global load issued so far (Q and tile 0) has landed before the
-    // loop, so waits inside the loop only ever cover the prefetch.
-    __builtin_amdgcn_s_waitcnt(0);
+    TileCursor lk = c3, lv = c2;   // next K and V tiles group 1 loads
     __syncthreads();
 
-    for (int it = 0; it < n_tiles; ++it) {
-        const int cur = it & 1;
-        // Prefetch the next tile (past the last tile the loads read zeros
-        // into the idle buffer; no branch needed).
-        load_tile(it + 1);
-        const int k0 = it * BN;
-        if (k0 < kw_end) {
-            if (k0 + BN <= kw_full) step(BoolTag<false>{}, cur, k0);
-            else step(BoolTag<true>{}, cur, k0);
-        }
-        store_tile(cur ^ 1);
+    TileCursor cur = c0;
+    bool act_prev = false;
+    if (grp == 1) __syncthreads();   // group 1 sits out the first phase
+    for (int t = 0;; ++t) {
+        const bool act = t < n_tiles && wave_active(cur);
+        // X(t): MFMAs.
+        if (act_prev) compute_pv((t - 1) & 1);
+        if (act) compute_s(t & 1);
+        if (t == n_tiles) break;
         __syncthreads();
+        // Y(t): softmax; group 1 also moves K(t+2), V(t+1) into LDS and
+        // starts the loads of K(t+3), V(t+2).
+        if (act) softmax(cur);
+        if (grp == 1) {
+            if (t + 2 < n_tiles) store_k(t & 1);
+            if (t + 1 < n_tiles) store_v((t + 1) & 1);
+            load_k(lk, t + 3 < n_tiles);
+            load_v(lv, t + 2 < n_tiles);
+            geo.advance(lk);
+            geo.advance(lv);
+        }
+        __syncthreads();
+        act_prev = act;
+        geo.advance(cur);
     }
+    if (grp == 0) __syncthreads();   // match group 1's extra first-phase barrier
 
     // Finish the row: l = both halves' sums; O = O / l; lse in natural log.
     const float l_tot = halves_sum(l_part);
@@ -355,12 +467,13 @@ __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int fl
 
     const int64_t row = (blk.b * a.S + blk.d * a.L + j) * a.H + blk.h;   // (b, slot, h) row index
     float wa = 0.f, wb = 1.f, l_out = lse_b;
-    if (flags & kFlagMerge) {
+    if (!kFused && (flags & kFlagMerge)) {
         const float la = a.lse_acc[row];
         merge_weights(la, lse_b, wa, wb, l_out);
     }
     wb *= inv;   // fold the normalisation into the partial's weight
     float* oa = a.o_acc + row * D;
+    const bool final_out = kFused || (flags & kFlagFinal);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -369,8 +482,8 @@ __global__ void __launch_bounds__(NT, 2) round_fwd_bf16_d128(RoundArgs a, int fl
             f32x4 ob = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
             f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
             if (wb != 0.f) r = wb * ob;
-            if ((flags & kFlagMerge) && wa != 0.f) r += wa * *(const f32x4*)(oa + dcol);
-            if (flags & kFlagFinal) {
+            if (!kFused && (flags & kFlagMerge) && wa != 0.f) r += wa * *(const f32x4*)(oa + dcol);
+            if (final_out) {
                 bf16x4 rb = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
                 *(bf16x4*)((bf16*)a.o_final + row * D + dcol) = rb;
             } else {
@@ -479,11 +592,14 @@ int flags_of(const RoundArgs& a) {
 
 }  // namespace
 
-hipError_t launch_round_bf16_d128(const RoundArgs& a, hipStream_t stream) {
+hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t stream) {
     const int64_t nqt = (a.L + BM - 1) / BM;
     const int64_t blocks = nqt * a.H * (a.dev_hi - a.dev_lo) * a.B;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(round_fwd_bf16_d128, dim3((unsigned)blocks), dim3(NT), 0, stream, a, flags_of(a));
+    if (fused)
+        hipLaunchKernelGGL(round_fwd_bf16_d128<true>, dim3((unsigned)blocks), dim3(NT), 0, stream, a, 0);
+    else
+        hipLaunchKernelGGL(round_fwd_bf16_d128<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, a, flags_of(a));
     return hipGetLastError();
 }
 

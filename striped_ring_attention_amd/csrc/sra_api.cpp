@@ -63,6 +63,11 @@ int check_desc(const sra_desc* d) {
         return fail(SRA_ERR_UNSUPPORTED, "no kernel for dtype %d with head_dim %lld (supported: bf16/128, f32/64, f32/128)",
                     d->dtype, (long long)d->head_dim);
     const int64_t L = d->seq / d->n_dev;
+    // Kernels address one device's slab of one head with 32-bit byte offsets
+    // (including one tile of look-ahead past its end).
+    const double slab = (double)(L + 2 * sra::kBf16TileK) * (double)d->heads * (double)d->head_dim * 4.0;
+    if (slab > 2147483647.0) return fail(SRA_ERR_UNSUPPORTED, "a device slab of %lld tokens x %lld heads is too large for 32-bit offsets",
+                                         (long long)L, (long long)d->heads);
     const int64_t tq = d->dtype == SRA_DTYPE_BF16 ? sra::kBf16TileQ : sra::kF32TileQ;
     const double blocks = (double)((L + tq - 1) / tq) * (double)d->heads * (double)d->n_dev * (double)d->batch;
     if (blocks > 2147483647.0) return fail(SRA_ERR_INVALID_ARG, "problem needs more than 2^31 workgroups per round");
@@ -87,8 +92,8 @@ sra::RoundArgs make_args(const sra_desc* d, const void* q, const void* k, const 
     return a;
 }
 
-hipError_t launch_round(const sra_desc* d, const sra::RoundArgs& a, hipStream_t s) {
-    if (d->dtype == SRA_DTYPE_BF16) return sra::launch_round_bf16_d128(a, s);
+hipError_t launch_round(const sra_desc* d, const sra::RoundArgs& a, hipStream_t s, bool fused = false) {
+    if (d->dtype == SRA_DTYPE_BF16) return sra::launch_round_bf16_d128(a, fused, s);
     return sra::launch_round_f32(a, d->head_dim, s);
 }
 
@@ -244,7 +249,8 @@ int sra_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float
 
 size_t sra_fwd_workspace_bytes(const sra_desc* desc) {
     if (check_desc(desc)) return 0;
-    if (desc->dtype == SRA_DTYPE_F32 || desc->n_dev == 1) return 0;   // fp32 accumulates in o itself
+    // fp32 accumulates in o itself; one round or the fused schedule needs no accumulator.
+    if (desc->dtype == SRA_DTYPE_F32 || desc->n_dev == 1 || desc->schedule == SRA_SCHEDULE_FUSED) return 0;
     return (size_t)(desc->batch * desc->seq * desc->heads * desc->head_dim) * sizeof(float);
 }
 
@@ -258,8 +264,8 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k, const 
         return fail(SRA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
     if (((uintptr_t)lse & 3u) || ((uintptr_t)live_counts & 7u))
         return fail(SRA_ERR_INVALID_ARG, "lse / live_counts misaligned");
-    if (desc->schedule == SRA_SCHEDULE_FUSED)
-        return fail(SRA_ERR_UNSUPPORTED, "the fused all-rounds schedule is not built");
+    if (desc->schedule == SRA_SCHEDULE_FUSED && desc->dtype != SRA_DTYPE_BF16)
+        return fail(SRA_ERR_UNSUPPORTED, "the fused all-rounds schedule is built for bf16 only");
     const size_t need = sra_fwd_workspace_bytes(desc);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(SRA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
@@ -281,6 +287,21 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k, const 
     const bool bf16 = desc->dtype == SRA_DTYPE_BF16;
     a.o_acc = bf16 ? (float*)workspace : (float*)o;
     a.o_final = o;
+    if (desc->schedule == SRA_SCHEDULE_FUSED) {
+        a.round = 0;
+        a.mode = 3;
+        if (round_events) {
+            hipError_t e = hipEventRecord((hipEvent_t)round_events[0], s);
+            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
+        }
+        hipError_t e = launch_round(desc, a, s, true);
+        if (e != hipSuccess) return hip_status(e, "fused ring launch");
+        if (round_events) {
+            e = hipEventRecord((hipEvent_t)round_events[1], s);
+            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
+        }
+        return SRA_OK;
+    }
     for (int r = 0; r < N; ++r) {
         a.round = r;
         if (bf16) a.mode = r == 0 ? (N == 1 ? 3 : 0) : (r == N - 1 ? 2 : 1);

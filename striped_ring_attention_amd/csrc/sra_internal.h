@@ -51,7 +51,7 @@ struct RoundArgs {
                          // 3: write the partial as the output (o_final, lse_acc)
 };
 
-hipError_t launch_round_bf16_d128(const RoundArgs& a, hipStream_t stream);
+hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t stream);
 hipError_t launch_round_f32(const RoundArgs& a, int64_t head_dim, hipStream_t stream);
 
 hipError_t launch_permute(const void* x, void* y, int64_t outer, int64_t seq, int64_t row_bytes,
@@ -60,7 +60,7 @@ hipError_t launch_permute(const void* x, void* y, int64_t outer, int64_t seq, in
 hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
                             int64_t rows, int64_t head_dim, hipStream_t stream);
 
-constexpr int kBf16TileQ = 128;
+constexpr int kBf16TileQ = 256;
 constexpr int kBf16TileK = 64;
 constexpr int kF32TileQ = 64;
 constexpr int kF32TileK = 16;
