@@ -110,7 +110,7 @@ def test_census_at_full_workload_sizes_closed_forms():
 
 
 def test_kernel_tiles(lib):
-    assert sra.kernel_tiles(torch.bfloat16, 128) == (128, 64)
+    assert sra.kernel_tiles(torch.bfloat16, 128) == (256, 64)
     assert sra.kernel_tiles(torch.float32, 64) == (64, 16)
     d = sra.make_desc(1, 64, 1, 64, 4, 1, sra.DTYPE_BF16)
     a, b = ctypes.c_int32(), ctypes.c_int32()
