@@ -1,20 +1,23 @@
 """Benchmark: striped ring-attention forward on one MI355X.
 
 One step = stripe-permute Q, K, V (original order -> striped device layout)
--> all N ring rounds (per-round kernels with the LSE merge fused, heaviest
-tiles first) -> unstripe O and LSE. Inputs are resident in HBM before the
-timed region. Prints one JSON line.
+-> all N ring rounds -> unstripe O and LSE. Inputs are resident in HBM before
+the timed region. The ring runs with the fused schedule by default (one
+launch walks every (round, key tile) pair, the log-sum-exp merge done
+online); the per-round schedule (one launch per ring round, merge fused in
+its epilogue) is timed alongside, as is the contiguous layout. Prints one
+JSON line.
 
 value  = useful causal TFLOP/s of the whole step: 4*Dh flops per live causal
          pair, B*H*S*(S+1)/2 pairs per step (masked pairs inside partial
          tiles and skipped tiles are not counted).
-roofline = the ring-round attention kernel (the dominant kernel): useful
-         flops of every launch in the timed region / the sum of their
-         durations, from HIP events recorded on the launch stream around
-         each launch, against the bf16 dense MFMA peak.
+roofline = the ring attention kernel (the dominant kernel): useful flops of
+         every launch in the timed region / the sum of their durations, from
+         HIP events recorded on the launch stream around each launch, against
+         the bf16 dense MFMA peak.
 cpu_baseline = the CPU oracle (fp64 numpy dense causal attention) on a
-         bounded sample of the same workload (whole sequence, a subset of
-         heads), rank 0 only.
+         bounded sample of the same workload (whole sequence, heads cycled
+         until about --cpu-seconds of work), rank 0 only.
 """
 
 import argparse
@@ -38,9 +41,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="short")
     ap.add_argument("--layout", default="striped", choices=["striped", "contiguous"])
+    ap.add_argument("--schedule", default="fused", choices=["fused", "per_round"],
+                    help="ring schedule of the timed step (the other one is timed alongside)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
-    ap.add_argument("--no-contiguous", action="store_true", help="skip the contiguous-layout comparison run")
+    ap.add_argument("--no-compare", action="store_true", help="skip the other-schedule and contiguous runs")
     return ap.parse_args()
 
 
@@ -55,7 +60,6 @@ def imbalance(live):
 
 def cpu_baseline(x, seconds):
     """Time the oracle on whole-sequence heads until ~`seconds` have elapsed."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -65,9 +69,9 @@ def cpu_baseline(x, seconds):
     q, k, v = (x[n].cpu() for n in ("q", "k", "v"))
     B, S, H, D = q.shape
     done, t_total = 0, 0.0
-    while done < H and t_total < seconds:
-        sl = slice(done, done + 1)
-        qh, kh, vh = (t[:, :, sl].double().numpy() for t in (q, k, v))
+    while t_total < seconds and done < 4 * H:
+        h = done % H
+        qh, kh, vh = (t[:, :, h:h + 1].double().numpy() for t in (q, k, v))
         t0 = time.perf_counter()
         oracle.dense_causal_attention(qh, kh, vh)
         t_total += time.perf_counter() - t0
@@ -75,8 +79,9 @@ def cpu_baseline(x, seconds):
     flops = 4.0 * D * B * done * S * (S + 1) / 2
     cores = len(os.sched_getaffinity(0))
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
-            "kind": "oracle", "sample": f"{done} of {H} heads, whole sequence S={S}, fp64 numpy dense causal "
-                                        f"attention, {t_total:.1f} s; host has {cores} cores available"}
+            "kind": "oracle", "sample": f"{done} head passes (heads cycled, {H} heads in the workload), whole "
+                                        f"sequence S={S}, fp64 numpy dense causal attention, {t_total:.1f} s; "
+                                        f"host has {cores} cores available"}
 
 
 def main():
@@ -102,6 +107,7 @@ def main():
         sys.exit(2)
     B, S, H, D, N = w["batch"], w["seq"], w["heads"], w["head_dim"], w["n_dev"]
     layout = sra.STRIPED if args.layout == "striped" else sra.CONTIGUOUS
+    sched = sra.SCHEDULE_FUSED if args.schedule == "fused" else sra.SCHEDULE_PER_ROUND
     dev = torch.device("cuda:0")
     x = make_inputs(args.workload, device=dev)
     q, k, v = x["q"], x["k"], x["v"]
@@ -109,10 +115,17 @@ def main():
     o_dev = torch.empty_like(q)
     lse_dev = torch.empty((B, S, H), dtype=torch.float32, device=dev)
     o, lse = torch.empty_like(q), torch.empty_like(lse_dev)
-    ws = torch.empty(max(1, sra.fwd_workspace_bytes(q, N, layout)), dtype=torch.uint8, device=dev)
+    ws_bytes = max(sra.fwd_workspace_bytes(q, N, lay, sc) for lay in (0, 1) for sc in (0, 1))
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     counts = torch.zeros(N * N, dtype=torch.int64, device=dev)
 
-    def step(events=None, perm_events=None, lay=layout, cnt=None):
+    def launches(sc):
+        return N if sc == sra.SCHEDULE_PER_ROUND else 1
+
+    def step(lay, sc, events=None, perm_events=None, cnt=None):
+        def ring(a, b, c, out, l_out):
+            sra.ring_attn_fwd(a, b, c, N, lay, schedule=sc, out=out, lse=l_out, workspace=ws, live_counts=cnt,
+                              round_events=events)
         if lay == sra.STRIPED:
             if perm_events:
                 perm_events[0].record()
@@ -120,8 +133,7 @@ def main():
                 sra.stripe_permute(src, N, out=dst)
             if perm_events:
                 perm_events[1].record()
-            sra.ring_attn_fwd(qd, kd, vd, N, lay, out=o_dev, lse=lse_dev, workspace=ws, live_counts=cnt,
-                              round_events=events)
+            ring(qd, kd, vd, o_dev, lse_dev)
             if perm_events:
                 perm_events[2].record()
             sra.unstripe(o_dev, N, out=o)
@@ -129,7 +141,7 @@ def main():
             if perm_events:
                 perm_events[3].record()
         else:
-            sra.ring_attn_fwd(q, k, v, N, lay, out=o, lse=lse, workspace=ws, live_counts=cnt, round_events=events)
+            ring(q, k, v, o, lse)
 
     def new_events(n):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -137,33 +149,41 @@ def main():
             e.record()          # create the underlying HIP event before its handle is passed on
         return evs
 
+    def timed(lay, sc, K, perm=False):
+        """K steps; returns (ms per step, kernel ms per launch list per step, permutation events)."""
+        nl = launches(sc)
+        evs = [new_events(2 * nl) for _ in range(K)]
+        pev = [new_events(4) for _ in range(K)] if perm else [None] * K
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(K):
+            step(lay, sc, events=[e.cuda_event for e in evs[i]], perm_events=pev[i])
+        t1.record()
+        torch.cuda.synchronize()
+        per_launch = [[evs[i][2 * r].elapsed_time(evs[i][2 * r + 1]) for r in range(nl)] for i in range(K)]
+        return t0.elapsed_time(t1) / K, per_launch, pev
+
     # Warm-up (and one counted pass for the device-side census).
-    step(cnt=counts)
+    step(layout, sched, cnt=counts)
     for _ in range(args.warmup):
-        step()
+        step(layout, sched)
     torch.cuda.synchronize()
 
     K = args.steps
-    round_ev = [new_events(2 * N) for _ in range(K)]
-    perm_ev = [new_events(4) for _ in range(K)] if layout == sra.STRIPED else [None] * K
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(K):
-        step(events=[e.cuda_event for e in round_ev[i]], perm_events=perm_ev[i])
-    t_end.record()
-    torch.cuda.synchronize()
+    ms_step, per_launch, perm_ev = timed(layout, sched, K, perm=(layout == sra.STRIPED))
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / K
-
-    attn_ms = sum(round_ev[i][2 * r].elapsed_time(round_ev[i][2 * r + 1]) for i in range(K) for r in range(N))
-    launch_ms = attn_ms / (K * N)
+    attn_ms = sum(sum(p) for p in per_launch) / K
+    nl = launches(sched)
     useful_flops = 4.0 * D * B * H * S * (S + 1) / 2
     value = useful_flops / (ms_step * 1e-3) / 1e12
-    attn_tflops = useful_flops * K / (attn_ms * 1e-3) / 1e12
+    attn_tflops = useful_flops / (attn_ms * 1e-3) / 1e12
     pairs = sra.count_live_pairs(S, N, layout).numpy() * (B * H)
-    per_launch_flops = [4.0 * D * float(pairs[r].sum()) for r in range(N)]
+    if sched == sra.SCHEDULE_PER_ROUND:
+        flops_per_launch = [4.0 * D * float(pairs[r].sum()) for r in range(N)]
+    else:
+        flops_per_launch = [useful_flops]
 
     perm = {}
     if layout == sra.STRIPED:
@@ -174,7 +194,7 @@ def main():
         u_bytes = 2 * (o.numel() * el + lse.numel() * 4)
         perm = {"stripe_permute_qkv_ms": p_ms, "stripe_permute_GBps": p_bytes / (p_ms * 1e-3) / 1e9,
                 "unstripe_o_lse_ms": u_ms, "unstripe_GBps": u_bytes / (u_ms * 1e-3) / 1e9,
-                "hbm_peak_GBps": PEAK_HBM_GBS}
+                "hbm_peak_GBps": PEAK_HBM_GBS, "note": "timed back to back inside the step (caches warm)"}
 
     # Imbalance: host census at 128x128 tiles and at the kernel's own tiles; device counters.
     tq, tk = sra.kernel_tiles(torch.bfloat16, D)
@@ -183,8 +203,8 @@ def main():
         live128 = sra.count_live_tiles(S, N, lay, 128, 128)[0].numpy()
         livek = sra.count_live_tiles(S, N, lay, tq, tk)[0].numpy()
         per, agg = imbalance(live128)
-        perk, aggk = imbalance(livek)
-        pp, pagg = imbalance(sra.count_live_pairs(S, N, lay).numpy())
+        _, aggk = imbalance(livek)
+        _, pagg = imbalance(sra.count_live_pairs(S, N, lay).numpy())
         imb[lname] = {"per_round_max_over_mean_128x128": per, "aggregate_128x128": agg,
                       f"aggregate_{tq}x{tk}_kernel_tiles": aggk, "aggregate_pairs": pagg}
     dev_counts = counts.view(N, N).cpu().numpy()
@@ -192,35 +212,42 @@ def main():
     imb["device_counters_match_host"] = bool(np.array_equal(dev_counts, host_counts))
     imb["device_per_round_max_over_mean"] = imbalance(dev_counts)[0]
 
-    # Contiguous layout, same work, for the striped-vs-contiguous comparison.
-    cmp = None
-    if layout == sra.STRIPED and not args.no_contiguous:
-        cev = [new_events(2 * N) for _ in range(K)]
-        torch.cuda.synchronize()
-        for i in range(K):
-            step(events=[e.cuda_event for e in cev[i]], lay=sra.CONTIGUOUS)
-        torch.cuda.synchronize()
-        c_ms = sum(cev[i][2 * r].elapsed_time(cev[i][2 * r + 1]) for i in range(K) for r in range(N)) / K
-        c_round = [sum(cev[i][2 * r].elapsed_time(cev[i][2 * r + 1]) for i in range(K)) / K for r in range(N)]
-        s_round = [sum(round_ev[i][2 * r].elapsed_time(round_ev[i][2 * r + 1]) for i in range(K)) / K
-                   for r in range(N)]
-        cmp = {"contiguous_ring_ms": c_ms, "striped_ring_ms": attn_ms / K,
-               "contiguous_useful_TFLOPs": useful_flops / (c_ms * 1e-3) / 1e12,
-               "striped_over_contiguous_speedup": c_ms / (attn_ms / K),
-               "striped_round_ms": s_round, "contiguous_round_ms": c_round}
+    compare = None
+    if not args.no_compare:
+        compare = {}
+        other = sra.SCHEDULE_PER_ROUND if sched == sra.SCHEDULE_FUSED else sra.SCHEDULE_FUSED
+        oname = "per_round" if other == sra.SCHEDULE_PER_ROUND else "fused"
+        for cname, lay, sc in ((f"{args.layout}_{oname}", layout, other),
+                               ("contiguous_per_round", sra.CONTIGUOUS, sra.SCHEDULE_PER_ROUND),
+                               ("contiguous_fused", sra.CONTIGUOUS, sra.SCHEDULE_FUSED)):
+            if lay == layout and sc == sched:
+                continue
+            step(lay, sc)
+            c_step, c_launch, _ = timed(lay, sc, K)
+            c_attn = sum(sum(p) for p in c_launch) / K
+            rec = {"ring_ms": c_attn, "ring_useful_TFLOPs": useful_flops / (c_attn * 1e-3) / 1e12,
+                   "step_ms": c_step}
+            if sc == sra.SCHEDULE_PER_ROUND:
+                rec["round_ms"] = [sum(c_launch[i][r] for i in range(K)) / K for r in range(N)]
+            compare[cname] = rec
+        compare[f"{args.layout}_{args.schedule}"] = {"ring_ms": attn_ms, "ring_useful_TFLOPs": attn_tflops,
+                                                     "step_ms": ms_step}
 
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "seq_len": S, "heads": H, "head_dim": D,
-                   "ring_devices": N, "layout": args.layout, "causal": True, "pass": "forward"},
+                   "ring_devices": N, "layout": args.layout, "schedule": args.schedule, "causal": True,
+                   "pass": "forward"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "round_fwd_bf16_d128", "avg_launch_ms": launch_ms,
-                     "flops_per_launch": per_launch_flops},
-        "imbalance": imb, "permutation": perm, "striped_vs_contiguous": cmp,
+                     "kernel": "round_fwd_bf16_d128<fused>" if sched == sra.SCHEDULE_FUSED
+                     else "round_fwd_bf16_d128<per-round>",
+                     "launches_per_step": nl, "avg_launch_ms": attn_ms / nl,
+                     "flops_per_launch": flops_per_launch},
+        "imbalance": imb, "permutation": perm, "compare": compare,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

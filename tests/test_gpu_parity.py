@@ -258,3 +258,47 @@ def test_fwd_mid_zero_query_closed_form(sra):
         e_o = float(np.abs(np64(o[:, :, heads]) - prefix).max())
         say(f"mid Q=0 layout={layout}: O {e_o:.3g} LSE {e_l:.3g}")
         assert e_o <= 2e-2 and e_l <= 2e-2
+
+
+# ---------------------------------------------------- fused all-rounds path --
+
+def run_full_fused(sra, x, n_dev, layout):
+    q, k, v = x["q"], x["k"], x["v"]
+    if layout == oracle.STRIPED:
+        q, k, v = (sra.stripe_permute(t, n_dev) for t in (q, k, v))
+    counts = torch.zeros(n_dev * n_dev, dtype=torch.int64, device=q.device)
+    o, lse = sra.ring_attn_fwd(q, k, v, n_dev, layout, schedule=sra.SCHEDULE_FUSED, live_counts=counts)
+    if layout == oracle.STRIPED:
+        o, lse = sra.unstripe(o, n_dev), sra.unstripe(lse, n_dev)
+    torch.cuda.synchronize()
+    return o, lse, counts.view(n_dev, n_dev).cpu()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fwd_short_bf16_fused_dense_parity(sra, short_case, layout):
+    w = WORKLOADS["short"]
+    x, o_ref, l_ref = short_case
+    o, lse, counts = run_full_fused(sra, x, w["n_dev"], layout)
+    e_o, e_l = maxabs(np64(o), o_ref), maxabs(np64(lse), l_ref)
+    say(f"short fused layout={layout}: O max-abs {e_o:.3g}  LSE {e_l:.3g}")
+    assert e_o <= 2e-2 and e_l <= 2e-2
+    assert torch.equal(o[:, 0], x["v"][:, 0])
+    assert torch.equal(counts, _census(sra, w["seq"], w["n_dev"], layout, torch.bfloat16, w["heads"]))
+    o2, l2, _ = run_full(sra, x, w["n_dev"], layout)        # per-round schedule, same inputs
+    assert (o.float() - o2.float()).abs().max().item() <= 2e-2
+    assert (lse - l2).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("S,N,H", [(8 * 200, 8, 2), (1024, 1, 2), (16, 16, 1), (4 * 300, 4, 3)])
+def test_fwd_fused_small_dense_parity(sra, S, N, H):
+    """Ragged shards (L not a multiple of the 256 x 64 tile), one device, one
+    token per device; both layouts."""
+    g = torch.Generator().manual_seed(S + N + H)
+    x = {n: (torch.randn((1, S, H, 128), generator=g) * 0.5).to(torch.bfloat16) for n in ("q", "k", "v")}
+    o_ref, l_ref = oracle.dense_causal_attention(x["q"], x["k"], x["v"])
+    xg = {n: t.cuda() for n, t in x.items()}
+    for layout in LAYOUTS:
+        o, lse, counts = run_full_fused(sra, xg, N, layout)
+        e_o, e_l = maxabs(np64(o), o_ref), maxabs(np64(lse), l_ref)
+        assert e_o <= 2e-2 and e_l <= 2e-2, (layout, e_o, e_l)
+        assert torch.equal(counts, _census(sra, S, N, layout, torch.bfloat16, H))
