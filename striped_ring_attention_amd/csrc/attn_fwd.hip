@@ -94,23 +94,33 @@ struct Decoded {
 };
 
 __device__ __forceinline__ Decoded decode_block(const RoundArgs& a, int64_t nqt) {
-    // Block order: query tiles fastest and heaviest first (the last query
-    // tile of a device has the most live keys), then heads, devices, batch.
-    // Workgroups are dealt to the 8 XCDs round-robin (block i on XCD i mod 8)
-    // and each XCD has its own L2, so hardware block i is remapped to logical
-    // block (i mod 8) * (n / 8) + i / 8: every XCD gets a contiguous range of
-    // logical blocks, and the query tiles that stream the same K/V slab run
-    // on the same XCD and share its L2.
-    const int64_t n = (int64_t)gridDim.x;
-    const int64_t n8 = n & ~(int64_t)7;
-    int64_t bid = blockIdx.x;
-    if (bid < n8) bid = (bid & 7) * (n8 >> 3) + (bid >> 3);
+    // Work items are (query tile, group), a group being one (batch, head,
+    // device); the last query tile of a device has the most live keys.
+    // Workgroups are dealt to the 8 XCDs round-robin (hardware block i runs
+    // on XCD i mod 8) and each XCD has its own L2. When the group count is a
+    // multiple of 8, XCD x owns groups [x*G/8, (x+1)*G/8) -- devices of a head
+    // adjacent, so the XCD's query tiles stream the same K/V slabs through
+    // its L2 -- and hands them out heaviest query tile first across all of
+    // its groups, which makes the hardware's greedy dispatch a
+    // longest-job-first schedule. Otherwise blocks map in plain order.
+    const int64_t nd = a.dev_hi - a.dev_lo;
+    const int64_t G = a.B * a.H * nd;
+    const int64_t i = blockIdx.x;
+    int64_t qi, g;
+    if ((G & 7) == 0) {
+        const int64_t gx = G >> 3;
+        const int64_t m = i >> 3;
+        qi = m / gx;
+        g = (i & 7) * gx + m % gx;
+    } else {
+        qi = i % nqt;
+        g = i / nqt;
+    }
     Decoded o;
-    int64_t qi = bid % nqt; bid /= nqt;
-    o.h = bid % a.H; bid /= a.H;
-    int64_t nd = a.dev_hi - a.dev_lo;
-    o.d = a.dev_lo + bid % nd; bid /= nd;
-    o.b = bid;
+    o.d = a.dev_lo + g % nd;
+    g /= nd;
+    o.h = g % a.H;
+    o.b = g / a.H;
     o.qt = nqt - 1 - qi;
     o.s = (o.d - a.round + a.N) % a.N;
     o.delta = live_delta(a.layout, a.N, a.L, o.d, o.s);
@@ -153,6 +163,11 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
 }
+
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
 
 // Walks the (round, key tile) pairs one workgroup visits, in ring order:
 // rounds r_lo .. r_hi-1, and within a round the key tiles of the source
@@ -200,10 +215,10 @@ struct RoundGeom {
 // for tile t-1, then S = K Q^T for tile t. In phase Y(t) it runs the softmax
 // of tile t on the vector ALU. Group 1 starts one phase late, so on every
 // SIMD one wave is in X while the other is in Y, and a workgroup barrier
-// separates consecutive phases. Group 1 also stages K/V tiles: in its Y(t)
-// it writes K(t+2) and V(t+1) (loaded two phases earlier) to LDS and issues
-// the global loads of K(t+3) and V(t+2). With K(t) read in X(t) of both
-// groups and V(t) in X(t+1) of both groups, two LDS buffers each suffice.
+// separates consecutive phases. In its Y(t) group 0 writes K(t+1) and
+// group 1 writes V(t+1) (each loaded two phases earlier) to LDS and starts
+// the loads of their part of tile t+2. With K(t) read in X(t) of both groups
+// and V(t) in X(t+1) of both groups, two LDS buffers each suffice.
 template <bool kFused>
 __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int flags) {
     __shared__ SmemBf16 sm;
@@ -269,52 +284,48 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     float l_part = 0.f;        // this half's share of the row sum
     const float sl = a.scale_log2;
 
-    // K/V staging by group 1 through buffer loads. Each tile gets its own
-    // buffer resource (base advanced to the tile's first row, size cut to what
-    // is left of the slab, both scalar), so the per-lane offsets are
-    // loop-invariant and rows past the slab end read as zero (their scores
-    // are masked and their V rows get weight 0).
+    // K/V staging through buffer loads: group 0 stages K tiles and group 1
+    // stages V tiles, one register tile each, loaded two phases before its
+    // data is written to LDS in the group's softmax phase. Each tile
+    // gets its own buffer resource (base advanced to the tile's first row,
+    // size cut to what is left of the slab, both scalar), so the per-lane
+    // offsets are loop-invariant and rows past the slab end read as zero
+    // (their scores are masked and their V rows get weight 0).
     //  K: thread -> (key row kr, 32-dim chunk kc), four 16-byte loads.
     //  V: thread -> (key quad kq, 8-dim chunk dc), one 16-byte load per key
     //     of the quad; each group of 16 lanes covers all 16 quads of one dim
     //     chunk, so the transposed LDS writes of a group fill one V^T row.
     const int kr = lt >> 2, kc = lt & 3;
     const int kq = lt & 15, dc = lt >> 4;
-    const int k_voff = kr * row_bytes + kc * 64;
-    const int v_voff = 4 * kq * row_bytes + dc * 16;
-    u32x4 kreg[4], vreg[4];
+    const int ld_voff = grp == 0 ? kr * row_bytes + kc * 64 : 4 * kq * row_bytes + dc * 16;
+    const int ld_step = grp == 0 ? 16 : row_bytes;   // between the four loads of a lane
+    const uint64_t ld_head = grp == 0 ? kv_head_k : kv_head_v;
+    u32x4 stg[4];
 
-    auto tile_rsrc = [&](uint64_t head, const TileCursor& c, bool valid) {
+    auto load_tile = [&](u32x4 (&dst)[4], const TileCursor& c, bool valid) {
         const int tile_off = c.kt * BN * row_bytes;
         int left = slab_bytes - tile_off;
         left = (valid && left > 0) ? left : 0;
-        return slab_rsrc((const void*)(head + (uint64_t)c.s * slab_stride + (uint64_t)tile_off), left);
-    };
-    auto load_k = [&](const TileCursor& c, bool valid) {
-        const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(kv_head_k, c, valid);
+        const __amdgpu_buffer_rsrc_t rsrc =
+            slab_rsrc((const void*)(ld_head + (uint64_t)c.s * slab_stride + (uint64_t)tile_off), left);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, k_voff + 16 * i, 0, 0);
+        for (int i = 0; i < 4; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_voff + i * ld_step, 0, 0);
     };
-    auto load_v = [&](const TileCursor& c, bool valid) {
-        const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(kv_head_v, c, valid);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[r] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, v_voff + r * row_bytes, 0, 0);
-    };
-    auto store_k = [&](int buf) {
+    auto store_k = [&](const u32x4 (&src)[4], int buf) {
         bf16* kd = &sm.k[buf][kr * KP + kc * 32];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(kd + 8 * i) = kreg[i];
+        for (int i = 0; i < 4; ++i) *(u32x4*)(kd + 8 * i) = src[i];
     };
     // V^T column of key quad kq: within each 16-key group the quads are
     // stored in the order [0, 2, 1, 3] (keys [0-3, 8-11, 4-7, 12-15]).
     const int vt_col = 16 * (kq >> 2) + 4 * ((kq & 1) * 2 + ((kq >> 1) & 1));
-    auto store_v = [&](int buf) {
-        // vreg[r][p] holds dims (2p, 2p+1) of key 4*kq + r.
+    auto store_v = [&](const u32x4 (&src)[4], int buf) {
+        // src[r][p] holds dims (2p, 2p+1) of key 4*kq + r.
         bf16* vd = &sm.vt[buf][(8 * dc) * VP + vt_col];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            uint2 lo = {pack_lo(vreg[0][p], vreg[1][p]), pack_lo(vreg[2][p], vreg[3][p])};
-            uint2 hi = {pack_hi(vreg[0][p], vreg[1][p]), pack_hi(vreg[2][p], vreg[3][p])};
+            uint2 lo = {pack_lo(src[0][p], src[1][p]), pack_lo(src[2][p], src[3][p])};
+            uint2 hi = {pack_hi(src[0][p], src[1][p]), pack_hi(src[2][p], src[3][p])};
             *(uint2*)(vd + (2 * p) * VP) = lo;
             *(uint2*)(vd + (2 * p + 1) * VP) = hi;
         }
@@ -418,18 +429,13 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     TileCursor c3 = c2;
     geo.advance(c3);
 
-    // Prologue (group 1): K(0), V(0) and K(1) into LDS; K(2), V(1) in flight.
-    if (grp == 1) {
-        load_k(c0, n_tiles > 0);
-        load_v(c0, n_tiles > 0);
-        store_k(0);
-        store_v(0);
-        load_k(c1, n_tiles > 1);
-        store_k(1);
-        load_k(c2, n_tiles > 2);
-        load_v(c1, n_tiles > 1);
-    }
-    TileCursor lk = c3, lv = c2;   // next K and V tiles group 1 loads
+    // Prologue: group 0 puts K(0) and group 1 puts V(0) into LDS buffer 0;
+    // tile 1 goes in flight in the staging registers.
+    load_tile(stg, c0, n_tiles > 0);
+    if (grp == 0) store_k(stg, 0);
+    else store_v(stg, 0);
+    load_tile(stg, c1, n_tiles > 1);
+    TileCursor ld = c2;   // next tile this wave's group loads
     __syncthreads();
 
     TileCursor cur = c0;
@@ -442,17 +448,17 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
         if (act) compute_s(t & 1);
         if (t == n_tiles) break;
         __syncthreads();
-        // Y(t): softmax; group 1 also moves K(t+2), V(t+1) into LDS and
-        // starts the loads of K(t+3), V(t+2).
+        // Y(t): softmax; the group's part of tile t+1 goes to LDS and the
+        // loads of its part of tile t+2 start. K(t+1) is first read in X(t+1)
+        // and its buffer's previous tile K(t-1) was last read in X(t-1);
+        // V(t+1) is first read in X(t+2) and V(t-1) was last read in X(t).
         if (act) softmax(cur);
-        if (grp == 1) {
-            if (t + 2 < n_tiles) store_k(t & 1);
-            if (t + 1 < n_tiles) store_v((t + 1) & 1);
-            load_k(lk, t + 3 < n_tiles);
-            load_v(lv, t + 2 < n_tiles);
-            geo.advance(lk);
-            geo.advance(lv);
+        if (t + 1 < n_tiles) {
+            if (grp == 0) store_k(stg, (t + 1) & 1);
+            else store_v(stg, (t + 1) & 1);
         }
+        load_tile(stg, ld, t + 2 < n_tiles);
+        geo.advance(ld);
         __syncthreads();
         act_prev = act;
         geo.advance(cur);
