@@ -176,6 +176,26 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k,
                       size_t workspace_bytes, int64_t* live_counts,
                       void* const* round_events, void* stream);
 
+/* Bytes of workspace sra_ring_attn_bwd needs for desc (fp32 [B, S, H]). */
+size_t sra_bwd_workspace_bytes(const sra_desc* desc);
+
+/* Gradient of the ring forward: every round for every device, bf16 with
+ * head_dim 128. Inputs in device layout: q, k, v, the forward's output o
+ * (dtype of desc), its fp32 lse, and the upstream gradient dout. Outputs dq,
+ * dk, dv (dtype of desc, device layout; fully overwritten). The pages train
+ * causal transformers with the method ("Key points": A100 and TPU results),
+ * which takes this pass: with P = exp(scale q.k - lse) on live pairs and
+ * Delta = rowsum(dout * o), dv = P^T dout, ds = P (dout v^T - Delta),
+ * dq = scale ds k, dk = scale ds^T q. In round r the K/V block of device s
+ * meets the queries of device (s + r) mod N; dk and dv of a block sum over
+ * rounds, dq of a device over the blocks it meets. Deterministic (no
+ * atomics). workspace: at least sra_bwd_workspace_bytes(desc) bytes.
+ * desc->schedule is ignored. Returns SRA_ERR_UNSUPPORTED for fp32. */
+int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k,
+                      const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,4 +51,5 @@ from .attention import (  # noqa: F401
     ring_attention,
     dense_causal_backward,
     backward_key_rows,
+    backward_query_rows,
 )

@@ -248,3 +248,36 @@ def backward_key_rows(q, k, v, do, key_rows, heads, scale=None):
                 dv[b, :, hn] += p.T @ dO
                 dk[b, :, hn] += sc * (ds.T @ Q)
     return dk, dv
+
+
+def backward_query_rows(q, k, v, do, rows, heads, scale=None):
+    """dQ for selected query positions and heads (for shapes where the dense
+    backward is too slow).
+
+    Row i needs its own forward quantities over keys k <= i: lse_i, O_i and
+    Delta_i = dO_i . O_i; then dS_ik = P_ik (dO_i . V_k - Delta_i) and
+    dQ_i = scale * sum_k dS_ik K_k. Each row costs O(i * D).
+    Returns dQ[B, len(rows), len(heads), D] float64.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    B, S, H, D = q.shape
+    sc = _scale(D, scale)
+    dq = np.zeros((B, len(rows), len(heads), D))
+    for b in range(B):
+        for hn, h in enumerate(heads):
+            for n, i in enumerate(rows):
+                i = int(i)
+                Qi = _f64(q[b, i, h])
+                dOi = _f64(do[b, i, h])
+                K = _f64(k[b, :i + 1, h])
+                V = _f64(v[b, :i + 1, h])
+                s = sc * (K @ Qi)
+                m = s.max()
+                e = np.exp(s - m)
+                den = e.sum()
+                p = e / den
+                Oi = p @ V
+                delta = float(dOi @ Oi)
+                ds = p * (V @ dOi - delta)
+                dq[b, n, hn] = sc * (ds @ K)
+    return dq

@@ -60,6 +60,9 @@ _PROTOS = {
     "sra_lse_merge": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "sra_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SraDesc)]),
     "sra_ring_attn_fwd": (_i32, [ctypes.POINTER(SraDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp, _vp]),
+    "sra_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SraDesc)]),
+    "sra_ring_attn_bwd": (_i32, [ctypes.POINTER(SraDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 ctypes.c_size_t, _vp]),
 }
 
 
@@ -235,6 +238,22 @@ def ring_attn_fwd(q, k, v, n_dev, layout, scale=0.0, schedule=SCHEDULE_PER_ROUND
     _check(lib().sra_ring_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                    _ptr(workspace), ws_bytes, _ptr(live_counts), ev, _stream()))
     return out, lse
+
+
+def ring_attn_bwd(q, k, v, o, lse, dout, n_dev, layout, scale=0.0, dq=None, dk=None, dv=None, workspace=None):
+    """Gradient of the ring forward on device-layout tensors; returns (dq, dk, dv)."""
+    _check_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    d = _desc_for(q, n_dev, layout, scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = lib().sra_bwd_workspace_bytes(ctypes.byref(d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().sra_ring_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream()))
+    return dq, dk, dv
 
 
 def striped_attention(q, k, v, n_dev, scale=0.0, schedule=SCHEDULE_PER_ROUND):

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsra.so")
 
-SOURCES = ["sra_api.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip"]
+SOURCES = ["sra_api.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -34,7 +34,7 @@ COMMON = [
 # Per-source flags. The attention kernels run with the IEEE mode bit off
 # (no NaN quieting around min/max; infinities still behave) so the row max
 # compiles to bare v_max3_f32.
-PER_SOURCE = {"attn_fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+PER_SOURCE = {n: ["-mno-amdgpu-ieee", "-fno-honor-nans"] for n in ("attn_fwd.hip", "attn_bwd.hip")}
 
 
 def _compile(src, extra):

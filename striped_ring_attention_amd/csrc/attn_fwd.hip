@@ -35,37 +35,15 @@
 //  * K and V tiles are double-buffered in LDS (row pitches padded so the
 //    16-byte reads of 8 consecutive lanes hit distinct banks); the next
 //    tile's global loads are in flight while the current tile computes.
-#include "sra_internal.h"
+#include "kernel_common.h"
 
 namespace sra {
 namespace {
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using namespace kc;
 
 constexpr int kFlagMerge = 1;   // merge with (o_acc, lse_acc) instead of overwriting them
 constexpr int kFlagFinal = 2;   // write the (merged) output to o_final in the input dtype
-
-constexpr float kLn2 = 0.693147180559945309f;
-
-
-// Reductions across the two 32-lane halves of a wavefront (lane l and l ^ 32).
-// v_permlane32_swap exchanges the upper half of its first operand with the
-// lower half of its second; with x in both, each lane receives {own, partner}
-// in its two results (in an order that depends on the half), so a symmetric
-// combination of the two is the two-lane reduction in every lane.
-__device__ __forceinline__ float halves_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Log-sum-exp merge weights (natural-log LSEs).
 __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, float& wb, float& l) {
@@ -80,58 +58,20 @@ __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, flo
     wb = eb * inv;
 }
 
-// A value the compiler cannot prove wave-uniform (it went through vector
-// registers) but that is: move it to scalar registers.
-__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ int64_t uniform_i64(int64_t x) { return (int64_t)uniform_u64((uint64_t)x); }
-
 struct Decoded {
     int64_t b, h, d, s, qt, delta;
 };
 
 __device__ __forceinline__ Decoded decode_block(const RoundArgs& a, int64_t nqt) {
-    // Work items are (query tile, group), a group being one (batch, head,
-    // device); the last query tile of a device has the most live keys.
-    // Workgroups are dealt to the 8 XCDs round-robin (hardware block i runs
-    // on XCD i mod 8) and each XCD has its own L2. When the group count is a
-    // multiple of 8, XCD x owns groups [x*G/8, (x+1)*G/8) -- devices of a head
-    // adjacent, so the XCD's query tiles stream the same K/V slabs through
-    // its L2 -- and hands them out heaviest query tile first across all of
-    // its groups, which makes the hardware's greedy dispatch a
-    // longest-job-first schedule. Otherwise blocks map in plain order.
-    const int64_t nd = a.dev_hi - a.dev_lo;
-    const int64_t G = a.B * a.H * nd;
-    const int64_t i = blockIdx.x;
-    int64_t qi, g;
-    if ((G & 7) == 0) {
-        const int64_t gx = G >> 3;
-        const int64_t m = i >> 3;
-        qi = m / gx;
-        g = (i & 7) * gx + m % gx;
-    } else {
-        qi = i % nqt;
-        g = i / nqt;
-    }
+    // Query tile heavy_rank 0 is the device's last (most live keys).
+    const WorkItem wi = decode_work(nqt, a.B, a.H, a.dev_hi - a.dev_lo, a.dev_lo);
     Decoded o;
-    o.d = a.dev_lo + g % nd;
-    g /= nd;
-    o.h = g % a.H;
-    o.b = g / a.H;
-    o.qt = nqt - 1 - qi;
-    o.s = (o.d - a.round + a.N) % a.N;
-    o.delta = live_delta(a.layout, a.N, a.L, o.d, o.s);
-    // The 64-bit divisions above are expanded on the vector ALU; the results
-    // are per-workgroup constants, so move them back to scalar registers.
-    o.b = uniform_i64(o.b);
-    o.h = uniform_i64(o.h);
-    o.d = uniform_i64(o.d);
-    o.s = uniform_i64(o.s);
-    o.qt = uniform_i64(o.qt);
-    o.delta = uniform_i64(o.delta);
+    o.b = wi.b;
+    o.h = wi.h;
+    o.d = wi.d;
+    o.qt = uniform_i64(nqt - 1 - wi.heavy_rank);
+    o.s = uniform_i64((o.d - a.round + a.N) % a.N);
+    o.delta = uniform_i64(live_delta(a.layout, a.N, a.L, o.d, o.s));
     return o;
 }
 
@@ -152,23 +92,6 @@ struct __align__(16) SmemBf16 {
     bf16 vt[2][D * VP];    // value tiles, dimension-major (transposed)
 };
 
-// Low (high) 16-bit halves of a and b packed as {a, b}: one v_perm_b32 each.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-// Buffer resource over (what is left of) one device's K or V slab of one
-// head: loads at offsets past `bytes` read as zero, so tile loads need
-// neither clamping nor branches.
-constexpr int kBufferFlags = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
-}
-
-template <bool B>
-struct BoolTag {
-    static constexpr bool value = B;
-};
-
 // Walks the (round, key tile) pairs one workgroup visits, in ring order:
 // rounds r_lo .. r_hi-1, and within a round the key tiles of the source
 // device that hold at least one live key for the workgroup's last query row.
@@ -178,16 +101,11 @@ struct TileCursor {
     int s, delta;         // source device of the round, live-key shift
 };
 
-// Live keys of local query row j (int32 form of live_keys; |delta| <= L + 1).
-__device__ __forceinline__ int live32(int j, int delta, int L) { return min(max(j + delta, 0), L); }
-
 struct RoundGeom {
     int L, N, layout, d, j_last, r_hi;
     __device__ __forceinline__ void enter(TileCursor& c) const {
         c.s = __builtin_amdgcn_readfirstlane((d - c.r + N) % N);
-        int64_t dl = live_delta(layout, N, L, d, c.s);
-        dl = dl < -(int64_t)L - 1 ? -(int64_t)L - 1 : (dl > (int64_t)L + 1 ? (int64_t)L + 1 : dl);
-        c.delta = __builtin_amdgcn_readfirstlane((int)dl);
+        c.delta = __builtin_amdgcn_readfirstlane(clamp_delta(live_delta(layout, N, L, d, c.s), L));
         c.nt = __builtin_amdgcn_readfirstlane((live32(j_last, c.delta, L) + BN - 1) / BN);
         c.kt = 0;
     }
@@ -299,7 +217,7 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     const int kq = lt & 15, dc = lt >> 4;
     const int ld_voff = grp == 0 ? kr * row_bytes + kc * 64 : 4 * kq * row_bytes + dc * 16;
     const int ld_step = grp == 0 ? 16 : row_bytes;   // between the four loads of a lane
-    const uint64_t ld_head = grp == 0 ? kv_head_k : kv_head_v;
+    const uint64_t ld_head = uniform_u64(grp == 0 ? kv_head_k : kv_head_v);   // wave-uniform
     u32x4 stg[4];
 
     auto load_tile = [&](u32x4 (&dst)[4], const TileCursor& c, bool valid) {

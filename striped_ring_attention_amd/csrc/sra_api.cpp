@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "sra_internal.h"
 
@@ -318,6 +319,60 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k, const 
         }
     }
     return SRA_OK;
+}
+
+size_t sra_bwd_workspace_bytes(const sra_desc* desc) {
+    if (check_desc(desc)) return 0;
+    return (size_t)(desc->batch * desc->seq * desc->heads) * sizeof(float);
+}
+
+int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int st = check_desc(desc);
+    if (st) return st;
+    if (desc->dtype != SRA_DTYPE_BF16)
+        return fail(SRA_ERR_UNSUPPORTED, "the backward is built for bf16 with head_dim 128 only");
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+        return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
+    for (const void* p : std::initializer_list<const void*>{q, k, v, o, dout, dq, dk, dv})
+        if (!aligned16(p)) return fail(SRA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if ((uintptr_t)lse & 3u) return fail(SRA_ERR_INVALID_ARG, "lse misaligned");
+    const size_t need = sra_bwd_workspace_bytes(desc);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SRA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if ((uintptr_t)workspace & 15u) return fail(SRA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    // Outputs must not overlap the inputs the kernels read.
+    const uintptr_t nbytes = (uintptr_t)(desc->batch * desc->seq * desc->heads * desc->head_dim * 2);
+    for (const void* out : std::initializer_list<const void*>{dq, dk, dv}) {
+        const uintptr_t a0 = (uintptr_t)out, a1 = a0 + nbytes;
+        for (const void* in : std::initializer_list<const void*>{q, k, v, o, dout}) {
+            const uintptr_t b0 = (uintptr_t)in, b1 = b0 + nbytes;
+            if (a0 < b1 && b0 < a1) return fail(SRA_ERR_INVALID_ARG, "a gradient overlaps an input");
+        }
+        const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
+        if (a0 < w1 && w0 < a1) return fail(SRA_ERR_INVALID_ARG, "a gradient overlaps the workspace");
+    }
+    sra::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.dout = dout;
+    a.delta = (float*)workspace;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = desc->batch;
+    a.S = desc->seq;
+    a.H = desc->heads;
+    a.L = desc->seq / desc->n_dev;
+    a.N = desc->n_dev;
+    a.layout = desc->layout;
+    a.scale = eff_scale(desc);
+    a.scale_log2 = (float)((double)a.scale * 1.4426950408889634074);
+    return hip_status(sra::launch_bwd_bf16_d128(a, (hipStream_t)stream), "ring backward launch");
 }
 
 }  // extern "C"

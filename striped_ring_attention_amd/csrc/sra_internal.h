@@ -52,6 +52,26 @@ struct RoundArgs {
 };
 
 hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t stream);
+
+// Backward of the whole ring (every round), bf16 with head dim 128.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;     // fp32 [B,S,H], natural log
+    const void* dout;
+    float* delta;         // fp32 [B,S,H] workspace: rowsum(dO * O)
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t B, S, H, L;
+    int32_t N, layout;
+    float scale;
+    float scale_log2;
+};
+
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_round_f32(const RoundArgs& a, int64_t head_dim, hipStream_t stream);
 
 hipError_t launch_permute(const void* x, void* y, int64_t outer, int64_t seq, int64_t row_bytes,

@@ -479,6 +479,18 @@ def test_backward_key_rows_matches_dense():
     np.testing.assert_allclose(dvs, dv[:, keys][:, :, heads], atol=1e-11)
 
 
+def test_backward_query_rows_matches_dense():
+    B, S, H, D = 1, 600, 3, 8
+    q, k, v, do = (rand((B, S, H, D), s) for s in (60, 61, 62, 63))
+    o, lse = oracle.dense_causal_attention(q, k, v)
+    dq, _, _ = oracle.dense_causal_backward(q, k, v, o, lse, do)
+    rows = np.array([0, 1, 299, 300, 599])
+    heads = [1, 2]
+    got = oracle.backward_query_rows(q, k, v, do, rows, heads)
+    np.testing.assert_allclose(got, dq[:, rows][:, :, heads], atol=1e-11)
+    assert np.abs(got[:, 0]).max() < 1e-14          # dQ_0 = 0: row 0 sees only its own key
+
+
 # --------------------------------------------------------- mutation tests --
 
 def _mutant(module_file, old, new):
