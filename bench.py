@@ -21,6 +21,7 @@ cpu_baseline = the CPU oracle (fp64 numpy dense causal attention) on a
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,16 @@ sys.path.insert(0, ROOT)
 METRIC = "useful causal attn TFLOP/s + % bf16 MFMA peak; striped vs contiguous max/mean"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
+# HBM traffic of one fused forward launch on the Short workload (striped),
+# from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by the same counters
+# on the stripe-permute copy kernel of known size; filled in from the counter
+# summary under profiles/ and valid only for the kernel sources it was taken on.
+TRAFFIC = {"workload": "short", "kernel_sources_sha256": "9b1f8772489b4b84c3cfafbb37a5ffff5c1dfb56ed4ddc5bab22749dabb21d29",
+           "bytes_per_launch": 1059188093,
+           "fetch_bytes_per_launch": 1013832325, "write_bytes_per_launch": 45355768,
+           "copy_scale": {"FETCH_SIZE": 1.99700, "WRITE_SIZE": 0.99974}}
 
 
 def parse():
@@ -46,6 +57,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-compare", action="store_true", help="skip the other-schedule and contiguous runs")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     return ap.parse_args()
 
 
@@ -84,6 +96,61 @@ def cpu_baseline(x, seconds):
                                         f"host has {cores} cores available"}
 
 
+def kernel_source_digest():
+    """sha256 over the sources the forward ring kernel is compiled from."""
+    h = hashlib.sha256()
+    for name in FWD_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "striped_ring_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload, sched, layout):
+    """HBM bytes per launch of the fused forward kernel from the last counter
+    runs, or None when they do not cover this configuration or the kernel's
+    sources have changed since they were taken."""
+    t = TRAFFIC
+    if (t is None or workload != t["workload"] or sched != 1 or layout != 1
+            or kernel_source_digest() != t["kernel_sources_sha256"]):
+        return None
+    return t["bytes_per_launch"]
+
+
+def traffic_detail(workload, sched, layout):
+    if stored_traffic(workload, sched, layout) is None:
+        return None
+    return {k: TRAFFIC[k] for k in ("fetch_bytes_per_launch", "write_bytes_per_launch", "copy_scale")}
+
+
+def time_backward(sra, torch, x, N, layout, fwd_step, qd, kd, vd, o_dev, lse_dev, o, lse, K, useful_fwd_flops):
+    """The ring backward (dQ, dK, dV) on the forward's device-layout outputs:
+    K launches of the three backward kernels, each bracketed by events on the
+    current stream. Useful flops: 10*Dh per live causal pair (S recomputed,
+    dP, dV, dQ, dK), i.e. 2.5x the forward's."""
+    fwd_step()
+    if layout == sra.STRIPED:
+        q, k, v, out, l = qd, kd, vd, o_dev, lse_dev
+        do = sra.stripe_permute(x["do"], N)
+    else:
+        q, k, v, out, l, do = x["q"], x["k"], x["v"], o, lse, x["do"]
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    ws = torch.empty(max(1, sra.bwd_workspace_bytes(q, N, layout)), dtype=torch.uint8, device=q.device)
+    for _ in range(2):
+        sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    flops = 2.5 * useful_fwd_flops
+    return {"ms": ms, "useful_TFLOPs": flops / (ms * 1e-3) / 1e12, "pct_bf16_peak": 100 * flops / (ms * 1e-3) / 1e12
+            / PEAK_BF16_TFLOPS, "flops_per_live_pair": "10*head_dim", "kernels": ["bwd_delta", "bwd_dq", "bwd_dkdv"],
+            "launches": K, "note": "not part of value: the headline metric is the forward"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -109,7 +176,7 @@ def main():
     layout = sra.STRIPED if args.layout == "striped" else sra.CONTIGUOUS
     sched = sra.SCHEDULE_FUSED if args.schedule == "fused" else sra.SCHEDULE_PER_ROUND
     dev = torch.device("cuda:0")
-    x = make_inputs(args.workload, device=dev)
+    x = make_inputs(args.workload, device=dev, with_grad=not args.no_backward)
     q, k, v = x["q"], x["k"], x["v"]
     qd, kd, vd = (torch.empty_like(t) for t in (q, k, v))
     o_dev = torch.empty_like(q)
@@ -233,6 +300,11 @@ def main():
         compare[f"{args.layout}_{args.schedule}"] = {"ring_ms": attn_ms, "ring_useful_TFLOPs": attn_tflops,
                                                      "step_ms": ms_step}
 
+    backward = None
+    if not args.no_backward:
+        backward = time_backward(sra, torch, x, N, layout, lambda: step(layout, sched), qd, kd, vd, o_dev, lse_dev,
+                                 o, lse, K, useful_flops)
+
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -242,12 +314,14 @@ def main():
                    "pass": "forward"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": stored_traffic(args.workload, sched, layout),
                      "kernel": "round_fwd_bf16_d128<fused>" if sched == sra.SCHEDULE_FUSED
                      else "round_fwd_bf16_d128<per-round>",
+                     "traffic_detail": traffic_detail(args.workload, sched, layout),
                      "launches_per_step": nl, "avg_launch_ms": attn_ms / nl,
                      "flops_per_launch": flops_per_launch},
-        "imbalance": imb, "permutation": perm, "compare": compare,
+        "imbalance": imb, "permutation": perm, "compare": compare, "backward": backward,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

@@ -173,6 +173,13 @@ def fwd_workspace_bytes(q, n_dev, layout, schedule=SCHEDULE_PER_ROUND):
     return lib().sra_fwd_workspace_bytes(ctypes.byref(d))
 
 
+def bwd_workspace_bytes(q, n_dev, layout):
+    """Workspace bytes sra_ring_attn_bwd needs for device-layout q (the per-row
+    Delta = rowsum(dO * O) vector)."""
+    d = _desc_for(q, n_dev, layout, 0.0)
+    return int(lib().sra_bwd_workspace_bytes(ctypes.byref(d)))
+
+
 # ------------------------------------------------------------------ device --
 
 def _row_bytes(x):

@@ -46,21 +46,22 @@ constexpr int KP = D + 8;     // row-major tile pitch in LDS (elements)
 
 // ------------------------------------------------------------------ Delta --
 
-// One thread per (b, slot, h) row: Delta = sum_c dO[c] * O[c] in fp32.
+// Sixteen lanes per (b, slot, h) row, each taking 8 consecutive elements
+// (16-byte loads, so a wave reads four whole 256-byte rows of O and of dO),
+// then a 16-lane butterfly sum: Delta = sum_c dO[c] * O[c] in fp32.
 __global__ void __launch_bounds__(256) bwd_delta(const bf16* __restrict__ o, const bf16* __restrict__ dout,
                                                  float* __restrict__ delta, uint64_t rows) {
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t r = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += stride) {
-        const bf16x8* a = (const bf16x8*)(o + r * D);
-        const bf16x8* b = (const bf16x8*)(dout + r * D);
+    const uint64_t stride = ((uint64_t)gridDim.x * blockDim.x) >> 4;
+    const int c = threadIdx.x & 15;
+    for (uint64_t r = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4; r < rows; r += stride) {
+        const bf16x8 x = *(const bf16x8*)(o + r * D + 8 * c);
+        const bf16x8 y = *(const bf16x8*)(dout + r * D + 8 * c);
         float s = 0.f;
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const bf16x8 x = a[c], y = b[c];
+        for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
-        }
-        delta[r] = s;
+        for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+        if (c == 0) delta[r] = s;
     }
 }
 
@@ -453,7 +454,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
 
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream) {
     const uint64_t rows = (uint64_t)(a.B * a.S * a.H);
-    uint64_t blocks = (rows + 255) / 256;
+    uint64_t blocks = (rows + 15) / 16;   // 16 rows per 256-thread block
     if (blocks > 256ull * 64) blocks = 256ull * 64;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(bwd_delta, dim3((unsigned)blocks), dim3(256), 0, stream, (const bf16*)a.o, (const bf16*)a.dout,
