@@ -34,7 +34,12 @@ COMMON = [
 # Per-source flags. The attention kernels run with the IEEE mode bit off
 # (no NaN quieting around min/max; infinities still behave) so the row max
 # compiles to bare v_max3_f32.
-PER_SOURCE = {n: ["-mno-amdgpu-ieee", "-fno-honor-nans"] for n in ("attn_fwd.hip", "attn_bwd.hip")}
+# The attention kernels run with IEEE mode off (v_max3 without NaN quieting)
+# and with the latency-oriented ILP scheduler, which keeps LDS operand reads a
+# step ahead of the MFMAs that consume them (the default occupancy-oriented
+# scheduler reuses one operand register set and waits on every read).
+PER_SOURCE = {n: ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+              for n in ("attn_fwd.hip", "attn_bwd.hip")}
 
 
 def _compile(src, extra):

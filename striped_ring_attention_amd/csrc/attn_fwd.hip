@@ -14,7 +14,7 @@
 // softmax results over disjoint key sets) and, on the driver's last round,
 // writes the output in the input dtype.
 //
-// bf16 kernel (Dh = 128): 4 wavefronts x 32 query rows = 128 rows per
+// bf16 kernel (Dh = 128): 8 wavefronts x 32 query rows = 256 rows per
 // workgroup, 64 keys per step.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: K is the A operand (32 keys x
 //    16 dims from LDS), Q^T the B operand (held in registers for the whole
@@ -22,19 +22,19 @@
 //    and 16 keys, so a query's row max and row sum are in-lane reductions
 //    plus one exchange between the two wave halves (v_permlane32_swap).
 //  * O^T = V^T P^T on the same instruction: P^T comes straight from the S^T
-//    accumulator registers (converted to bf16); V^T is the A operand read
-//    from an LDS copy of the V tile stored dimension-major, with the keys of
-//    each 16-key group ordered [0-3, 8-11, 4-7, 12-15] so that one 16-byte
-//    LDS read gives the 8 keys a lane's P^T registers hold. The O^T
-//    accumulator keeps one query per lane, so the softmax rescale is
-//    per-lane too.
+//    accumulator registers (converted to bf16); the V^T operand is read from
+//    the key-major V tile with ds_read_b64_tr_b16, which transposes 16-bit
+//    elements across groups of 16 lanes, so each lane receives the keys its
+//    P^T registers hold for one head dimension. The O^T accumulator keeps one
+//    query per lane, so the softmax rescale is per-lane too.
 //  * Softmax runs in the log2 domain with v_exp_f32. The running offset is
 //    only raised when a tile's max exceeds it by more than 2^8 (the result
 //    does not depend on the offset; it only bounds p <= 256), so the
 //    64-register rescale of O is rare.
-//  * K and V tiles are double-buffered in LDS (row pitches padded so the
-//    16-byte reads of 8 consecutive lanes hit distinct banks); the next
-//    tile's global loads are in flight while the current tile computes.
+//  * K and V tiles go from HBM straight into a 4-stage LDS ring
+//    (buffer_load ... lds, no register staging), three tiles ahead of use;
+//    16-byte chunks are XOR-swizzled per row so both MFMA operand read
+//    patterns are bank-conflict-free.
 #include "kernel_common.h"
 
 namespace sra {
@@ -81,16 +81,57 @@ constexpr int D = 128;
 constexpr int BM = kBf16TileQ;   // 256 query rows per workgroup: 8 wavefronts x 32
 constexpr int BN = kBf16TileK;   // 64 keys per tile
 constexpr int NT = 512;          // 8 wavefronts in two groups of 4: one wave of each group per SIMD
-constexpr int KP = D + 8;        // K tile row pitch in LDS (elements)
-constexpr int VP = BN + 8;       // V^T tile row pitch in LDS (elements)
+constexpr int NS = 4;             // K/V tile stages in LDS
 constexpr float kTau = 8.0f;     // lazy-rescale threshold (log2 units)
 
-static_assert(BM == 256 && BN == 64 && NT == 512, "thread mappings below assume these");
+static_assert(BM == 256 && BN == 64 && NT == 512 && D == 128, "thread mappings below assume these");
 
+// K and V tiles, key-major (256-byte rows, no padding: the loads write LDS
+// directly), with the 16-byte chunks of each row XOR-swizzled so that the
+// MFMA operand reads are bank-conflict-free:
+//   K: chunk c of key row r sits in slot c ^ (r & 15)
+//   V: chunk c of key row r sits in slot c ^ (4 * (r & 3))
 struct __align__(16) SmemBf16 {
-    bf16 k[2][BN * KP];    // key tiles, row-major
-    bf16 vt[2][D * VP];    // value tiles, dimension-major (transposed)
+    bf16 k[NS][BN * D];
+    bf16 v[NS][BN * D];
 };
+
+// Workgroup barrier without a memory fence. The K/V loads write LDS
+// asynchronously; a fenced barrier would make every wave wait for all of its
+// loads in flight, which is exactly what the deep prefetch avoids. Ordering
+// is explicit instead: a loading wave waits for its own loads of a tile
+// (vmcnt) before the barrier that precedes the tile's first read, and LDS
+// reads are complete (lgkmcnt) before the barriers after which their buffer
+// can be refilled.
+__device__ __forceinline__ void bar() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+// expcnt in 6:4, lgkmcnt in 11:8; a field at its maximum is not waited on.
+constexpr int kWaitLgkm0 = 0xC07F;                // lgkmcnt(0)
+constexpr int kWaitVm4 = 0x0F74;                  // vmcnt(4)
+constexpr int kWaitVm8 = 0x0F78;                  // vmcnt(8)
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One buffer_load_dwordx4 ... lds: lane l's 16 bytes at buffer offset voff go
+// to LDS byte lds + 16 l (LDS base in M0). Issued from inline assembly so that
+// the compiler's wait insertion, which would otherwise make every later LDS
+// read wait for all loads in flight, leaves the loads alone; their
+// completion is awaited explicitly (vmcnt) before the barrier that publishes
+// the tile.
+__device__ __forceinline__ void load_lds_b128(i32x4 rsrc, int voff, uint32_t lds) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define SRA_LDS4(p) ((__attribute__((address_space(3))) s16x4*)(p))
 
 // Walks the (round, key tile) pairs one workgroup visits, in ring order:
 // rounds r_lo .. r_hi-1, and within a round the key tiles of the source
@@ -131,12 +172,10 @@ struct RoundGeom {
 // Schedule ("ping-pong"): the two groups of 4 wavefronts run the same tile
 // sequence one phase apart. In phase X(t) a wave issues its MFMAs: O += P V
 // for tile t-1, then S = K Q^T for tile t. In phase Y(t) it runs the softmax
-// of tile t on the vector ALU. Group 1 starts one phase late, so on every
-// SIMD one wave is in X while the other is in Y, and a workgroup barrier
-// separates consecutive phases. In its Y(t) group 0 writes K(t+1) and
-// group 1 writes V(t+1) (each loaded two phases earlier) to LDS and starts
-// the loads of their part of tile t+2. With K(t) read in X(t) of both groups
-// and V(t) in X(t+1) of both groups, two LDS buffers each suffice.
+// of tile t on the vector ALU. Group 1 starts one phase late, and waves w and
+// w+4 share a SIMD, so on every SIMD one wave is in X while the other is in
+// Y; a workgroup barrier separates consecutive phases. In its Y(t) group 0
+// starts the loads of K(t+3) and group 1 those of V(t+3).
 template <bool kFused>
 __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int flags) {
     __shared__ SmemBf16 sm;
@@ -145,9 +184,8 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     const Decoded blk = decode_block(a, nqt);
     const int L = (int)a.L;   // the host bounds L * H * D so that in-slab offsets fit in 32 bits
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
     const int grp = w >> 2;
-    const int lt = tid & 255;   // loader thread index within group 1
 
     const int j0 = (int)blk.qt * BM;
     const int j1 = min(j0 + BM, L);
@@ -202,89 +240,88 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     float l_part = 0.f;        // this half's share of the row sum
     const float sl = a.scale_log2;
 
-    // K/V staging through buffer loads: group 0 stages K tiles and group 1
-    // stages V tiles, one register tile each, loaded two phases before its
-    // data is written to LDS in the group's softmax phase. Each tile
-    // gets its own buffer resource (base advanced to the tile's first row,
-    // size cut to what is left of the slab, both scalar), so the per-lane
-    // offsets are loop-invariant and rows past the slab end read as zero
-    // (their scores are masked and their V rows get weight 0).
-    //  K: thread -> (key row kr, 32-dim chunk kc), four 16-byte loads.
-    //  V: thread -> (key quad kq, 8-dim chunk dc), one 16-byte load per key
-    //     of the quad; each group of 16 lanes covers all 16 quads of one dim
-    //     chunk, so the transposed LDS writes of a group fill one V^T row.
-    const int kr = lt >> 2, kc = lt & 3;
-    const int kq = lt & 15, dc = lt >> 4;
-    const int ld_voff = grp == 0 ? kr * row_bytes + kc * 64 : 4 * kq * row_bytes + dc * 16;
-    const int ld_step = grp == 0 ? 16 : row_bytes;   // between the four loads of a lane
-    const uint64_t ld_head = uniform_u64(grp == 0 ? kv_head_k : kv_head_v);   // wave-uniform
-    u32x4 stg[4];
+    // K/V staging: each tile is loaded straight into LDS (buffer_load ...
+    // lds: lane l of an instruction writes bytes [16 l, 16 l + 16) after the
+    // instruction's LDS base, from any global address the lane names). Group 0
+    // loads K tiles and group 1 V tiles; wave wg of a group issues four
+    // instructions per tile, instruction q covering key rows 4 wg + 16 q .. +3.
+    // Lane l writes key row 4 wg + 16 q + l/16, LDS slot l % 16, so it loads
+    // the global chunk that the slot holds under the swizzle. Each tile gets
+    // its own buffer resource (base at the tile's first row, size cut to what
+    // is left of the slab): the lane offsets are loop-invariant and rows past
+    // the slab end are not read (their scores are masked and their V rows get
+    // weight 0; LDS is zeroed once at the start so such rows hold finite data).
+    const int wg = w & 3;
+    const int ld_row = 4 * wg + (lane >> 4);
+    const int ld_sw = grp == 0 ? (ld_row & 15) : 4 * (lane >> 4);
+    const int ld_voff = ld_row * row_bytes + 16 * ((lane & 15) ^ ld_sw);
+    const int ld_step = 16 * row_bytes;
+    const uint64_t ld_head = uniform_u64(grp == 0 ? kv_head_k : kv_head_v);
+    bf16* const ld_lds0 = (grp == 0 ? &sm.k[0][0] : &sm.v[0][0]) + 512 * wg;
 
-    auto load_tile = [&](u32x4 (&dst)[4], const TileCursor& c, bool valid) {
+    auto load_tile = [&](const TileCursor& c, bool valid, int stage) {
         const int tile_off = c.kt * BN * row_bytes;
         int left = slab_bytes - tile_off;
         left = (valid && left > 0) ? left : 0;
-        const __amdgpu_buffer_rsrc_t rsrc =
-            slab_rsrc((const void*)(ld_head + (uint64_t)c.s * slab_stride + (uint64_t)tile_off), left);
+        const uint64_t base = ld_head + (uint64_t)c.s * slab_stride + (uint64_t)tile_off;
+        const i32x4 rsrc = {(int)(uint32_t)base, (int)(uint32_t)(base >> 32) & 0xFFFF, left, kBufferFlags};
+        const uint32_t dst = lds_addr(ld_lds0 + stage * (BN * D));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ld_voff + i * ld_step, 0, 0);
-    };
-    auto store_k = [&](const u32x4 (&src)[4], int buf) {
-        bf16* kd = &sm.k[buf][kr * KP + kc * 32];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(kd + 8 * i) = src[i];
-    };
-    // V^T column of key quad kq: within each 16-key group the quads are
-    // stored in the order [0, 2, 1, 3] (keys [0-3, 8-11, 4-7, 12-15]).
-    const int vt_col = 16 * (kq >> 2) + 4 * ((kq & 1) * 2 + ((kq >> 1) & 1));
-    auto store_v = [&](const u32x4 (&src)[4], int buf) {
-        // src[r][p] holds dims (2p, 2p+1) of key 4*kq + r.
-        bf16* vd = &sm.vt[buf][(8 * dc) * VP + vt_col];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint2 lo = {pack_lo(src[0][p], src[1][p]), pack_lo(src[2][p], src[3][p])};
-            uint2 hi = {pack_hi(src[0][p], src[1][p]), pack_hi(src[2][p], src[3][p])};
-            *(uint2*)(vd + (2 * p) * VP) = lo;
-            *(uint2*)(vd + (2 * p + 1) * VP) = hi;
-        }
+        for (int q = 0; q < 4; ++q) load_lds_b128(rsrc, ld_voff + q * ld_step, dst + 4096 * q);
     };
 
-    // S^T = K Q^T over the K tile in buffer `buf`: sacc[kb] holds keys
-    // kb*32 .. kb*32+31 of the tile against this wave's 32 queries.
+    // S^T = K Q^T over the K tile in `stage`: sacc[kb] holds keys
+    // kb*32 .. kb*32+31 of the tile against this wave's 32 queries. Lane
+    // (c32, h2) reads chunk 2 kk + h2 of key row 32 kb + c32.
     f32x16 sacc[2];
-    auto compute_s = [&](int buf) {
-        const bf16* ks = sm.k[buf] + c32 * KP + 8 * h2;
+    auto compute_s = [&](int stage) {
+        const bf16* ks = sm.k[stage] + c32 * D;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            const bf16x8 k0f = *(const bf16x8*)(ks + kk * 16);
-            const bf16x8 k1f = *(const bf16x8*)(ks + 32 * KP + kk * 16);
+            const int slot = (2 * kk + h2) ^ (c32 & 15);
+            const bf16x8 k0f = *(const bf16x8*)(ks + 8 * slot);
+            const bf16x8 k1f = *(const bf16x8*)(ks + 32 * D + 8 * slot);
             sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qreg[kk], kk == 0 ? f32x16{} : sacc[0], 0, 0, 0);
             sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qreg[kk], kk == 0 ? f32x16{} : sacc[1], 0, 0, 0);
         }
     };
 
-    // O^T += V^T P^T over the V tile in buffer `buf`, after applying the
-    // pending rescale of O (rare: only when the running offset was raised).
+    // O^T += V^T P^T over the V tile in `stage`, after applying the pending
+    // rescale of O (rare: only when the running offset was raised).
+    // The V^T operand comes from the key-major tile through ds_read_b64_tr_b16:
+    // within each 16-lane group, lane i receives element i % 4 of the 8-byte
+    // pieces named by lanes 4v + i / 4 (v = 0..3). Lane (g = l / 16, j = l % 16)
+    // names key 16 kk + 8 rd + 4 (g / 2) + j / 4, dims 32 db + 16 (g % 2) +
+    // 4 (j % 4) .. +3, so lane l collects dim 32 db + l % 32 of keys
+    // 16 kk + 8 rd + 4 h2 + 0..3 -- the keys its P^T registers hold
+    // (16-key step kk uses keys 16 kk + [4 h2 .. 4 h2 + 3] and
+    // 16 kk + 8 + [4 h2 .. 4 h2 + 3] of the S^T accumulator).
     bf16x8 pop[2][2];
     bool resc = false;
     float alpha_p = 1.f;
-    auto compute_pv = [&](int buf) {
+    const int tg = lane >> 4, tj = lane & 15;
+    const int tr_row = 4 * (tg >> 1) + (tj >> 2);
+    const int tr_lo = 8 * (2 * (tg & 1) + ((tj & 3) >> 1)) + 4 * (tj & 1);   // element offset in the slot group
+    auto compute_pv = [&](int stage) {
         if (resc) {
 #pragma unroll
             for (int db = 0; db < 4; ++db) oacc[db] *= alpha_p;
         }
-        const bf16* vts = sm.vt[buf] + c32 * VP + 8 * h2;
+        const bf16* vs = sm.v[stage] + tr_row * D + tr_lo;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 vf[4];
 #pragma unroll
-            for (int kk2 = 0; kk2 < 2; ++kk2) {
-                bf16x8 vf[4];
-#pragma unroll
-                for (int db = 0; db < 4; ++db) vf[db] = *(const bf16x8*)(vts + db * 32 * VP + kb * 32 + kk2 * 16);
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pop[kb][kk2], oacc[db], 0, 0, 0);
+            for (int db = 0; db < 4; ++db) {
+                const bf16* p = vs + 32 * (db ^ (tj >> 2)) + kk * 16 * D;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(p));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(p + 8 * D));
+                const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                vf[db] = __builtin_bit_cast(bf16x8, both);
             }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pop[kk >> 1][kk & 1], oacc[db], 0, 0, 0);
         }
     };
 
@@ -344,44 +381,51 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     geo.advance(c1);
     TileCursor c2 = c1;
     geo.advance(c2);
-    TileCursor c3 = c2;
-    geo.advance(c3);
+    TileCursor ld = c2;
+    geo.advance(ld);
 
-    // Prologue: group 0 puts K(0) and group 1 puts V(0) into LDS buffer 0;
-    // tile 1 goes in flight in the staging registers.
-    load_tile(stg, c0, n_tiles > 0);
-    if (grp == 0) store_k(stg, 0);
-    else store_v(stg, 0);
-    load_tile(stg, c1, n_tiles > 1);
-    TileCursor ld = c2;   // next tile this wave's group loads
-    __syncthreads();
+    // Zero the stages once (rows past a slab end are never loaded), then put
+    // tiles 0, 1, 2 in flight and wait for tile 0.
+    {
+        u32x4* z = (u32x4*)&sm;
+        for (int i = tid; i < (int)(sizeof(SmemBf16) / 16); i += NT) z[i] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bar();
+    }
+    load_tile(c0, n_tiles > 0, 0);
+    load_tile(c1, n_tiles > 1, 1);
+    load_tile(c2, n_tiles > 2, 2);
+    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    bar();
 
+    // Main loop. Phase X(t): MFMAs (P V of tile t-1, then S of tile t).
+    // Phase Y(t): softmax of tile t; the group waits for its part of tile t+1
+    // and starts the loads of its part of tile t+3 into the stage of tile t-1.
+    // Stage reuse: K(t-1) was last read in X(t-1) of group 1, V(t-1) in X(t)
+    // of group 1 -- both before the barrier that opens the loading group's
+    // Y(t). Tile t+1's K is first read in X(t+1) and its V in X(t+2), both
+    // after the barrier that closes the loading group's Y(t).
     TileCursor cur = c0;
     bool act_prev = false;
-    if (grp == 1) __syncthreads();   // group 1 sits out the first phase
+    if (grp == 1) bar();   // group 1 sits out the first phase
     for (int t = 0;; ++t) {
         const bool act = t < n_tiles && wave_active(cur);
-        // X(t): MFMAs.
-        if (act_prev) compute_pv((t - 1) & 1);
-        if (act) compute_s(t & 1);
+        if (act_prev) compute_pv((t - 1) & (NS - 1));
+        if (act) compute_s(t & (NS - 1));
         if (t == n_tiles) break;
-        __syncthreads();
-        // Y(t): softmax; the group's part of tile t+1 goes to LDS and the
-        // loads of its part of tile t+2 start. K(t+1) is first read in X(t+1)
-        // and its buffer's previous tile K(t-1) was last read in X(t-1);
-        // V(t+1) is first read in X(t+2) and V(t-1) was last read in X(t).
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bar();
         if (act) softmax(cur);
-        if (t + 1 < n_tiles) {
-            if (grp == 0) store_k(stg, (t + 1) & 1);
-            else store_v(stg, (t + 1) & 1);
-        }
-        load_tile(stg, ld, t + 2 < n_tiles);
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        load_tile(ld, t + 3 < n_tiles, (t + 3) & (NS - 1));
         geo.advance(ld);
-        __syncthreads();
+        bar();
         act_prev = act;
         geo.advance(cur);
     }
-    if (grp == 0) __syncthreads();   // match group 1's extra first-phase barrier
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (grp == 0) bar();   // match group 1's extra first-phase barrier
+    __builtin_amdgcn_s_waitcnt(0);   // no load may still be writing LDS when the workgroup ends
 
     // Finish the row: l = both halves' sums; O = O / l; lse in natural log.
     const float l_tot = halves_sum(l_part);
