@@ -39,10 +39,10 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by the same counters
 # on the stripe-permute copy kernel of known size; filled in from the counter
 # summary under profiles/ and valid only for the kernel sources it was taken on.
-TRAFFIC = {"workload": "short", "kernel_sources_sha256": "9b1f8772489b4b84c3cfafbb37a5ffff5c1dfb56ed4ddc5bab22749dabb21d29",
-           "bytes_per_launch": 1059188093,
-           "fetch_bytes_per_launch": 1013832325, "write_bytes_per_launch": 45355768,
-           "copy_scale": {"FETCH_SIZE": 1.99700, "WRITE_SIZE": 0.99974}}
+TRAFFIC = {"workload": "short", "kernel_sources_sha256": "44efbe1d32557bfe430094a26be3efc56df27184e80507a9ba570ce1723a51e5",
+           "bytes_per_launch": 1032637329,
+           "fetch_bytes_per_launch": 996751043, "write_bytes_per_launch": 35886286,
+           "copy_scale": {"FETCH_SIZE": 1.99700, "WRITE_SIZE": 0.99953}}
 
 
 def parse():
@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-compare", action="store_true", help="skip the other-schedule and contiguous runs")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-critical-path", action="store_true",
+                    help="skip the per-(device, round) timing of the simulated ring")
     return ap.parse_args()
 
 
@@ -300,6 +302,17 @@ def main():
         compare[f"{args.layout}_{args.schedule}"] = {"ring_ms": attn_ms, "ring_useful_TFLOPs": attn_tflops,
                                                      "step_ms": ms_step}
 
+    critical = None
+    if not args.no_critical_path:
+        from striped_ring_attention_amd import ring_sim
+        t_c = ring_sim.time_device_rounds(q, k, v, N, sra.CONTIGUOUS, reps=3)
+        for src, dst in ((q, qd), (k, kd), (v, vd)):
+            sra.stripe_permute(src, N, out=dst)
+        t_s = ring_sim.time_device_rounds(qd, kd, vd, N, sra.STRIPED, reps=3)
+        critical = ring_sim.project(t_s, t_c, ring_sim.kv_block_bytes(B, S, H, D, N, q.element_size()))
+        critical["note"] = ("one launch per (device, round) on this GPU; ring time = sum over rounds of "
+                            "max(slowest device, K/V transfer at the assumed link bandwidth)")
+
     backward = None
     if not args.no_backward:
         backward = time_backward(sra, torch, x, N, layout, lambda: step(layout, sched), qd, kd, vd, o_dev, lse_dev,
@@ -322,6 +335,7 @@ def main():
                      "launches_per_step": nl, "avg_launch_ms": attn_ms / nl,
                      "flops_per_launch": flops_per_launch},
         "imbalance": imb, "permutation": perm, "compare": compare, "backward": backward,
+        "critical_path": critical,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

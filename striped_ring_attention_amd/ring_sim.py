@@ -1,0 +1,129 @@
+"""Simulated N-device ring from one-GPU measurements.
+
+Striped Attention summary page (research.elamur.ai), "Summary" paragraph 1:
+every ring round, each device attends its queries to the K/V block it holds
+and passes the block on, so a round lasts as long as its slowest device; with
+contiguous chunks the causal mask leaves some devices with little or no work
+in a round while others have a full block ("Key points", Imbalance). The
+striped layout gives every device the same share in every round ("Summary"
+paragraph 2). On one MI355X each (device d, round r) unit of work is launched
+alone (``sra_ring_round_attn`` with a device filter, one GPU standing in for
+one ring device) and timed; then
+
+    ring time      = sum_r max(max_d t(d, r), t_comm)
+    compute bound  = sum_r max_d t(d, r)
+
+where t_comm is the time to pass one K/V block to the next device, overlapped
+with the round's compute (a stated model, not a measurement: the pages name
+no interconnect and this build runs on one GPU). The projected speedup of
+striped over contiguous is the ratio of ring times at the same shape.
+
+Host-side functions (``critical_path``, ``ring_time``, ``kv_block_bytes``,
+``project``) are plain Python; ``time_device_rounds`` needs the GPU library.
+"""
+
+import argparse
+import json
+import statistics
+
+DEFAULT_LINK_GBPS = 153.0   # assumed bandwidth of one device-to-device link, GB/s
+
+
+def critical_path(t):
+    """sum over rounds of the slowest device's time; t[r][d]."""
+    return float(sum(max(row) for row in t))
+
+
+def ring_time(t, t_comm):
+    """Ring time when each round's K/V transfer (t_comm) overlaps its compute."""
+    return float(sum(max(max(row), t_comm) for row in t))
+
+
+def mean_path(t):
+    """sum over rounds of the mean device time: the time if work were perfectly balanced."""
+    return float(sum(sum(row) / len(row) for row in t))
+
+
+def kv_block_bytes(batch, seq, heads, head_dim, n_dev, elem_bytes=2):
+    """Bytes of one device's K and V block (what one ring hop carries)."""
+    return 2 * batch * (seq // n_dev) * heads * head_dim * elem_bytes
+
+
+def project(t_striped, t_contig, block_bytes, link_gbps=DEFAULT_LINK_GBPS):
+    """Projected ring times and speedups from per-(round, device) times in ms."""
+    t_comm = block_bytes / (link_gbps * 1e9) * 1e3
+    out = {"t_comm_ms": t_comm, "link_GBps": link_gbps, "kv_block_bytes": block_bytes}
+    for name, t in (("striped", t_striped), ("contiguous", t_contig)):
+        out[name] = {"critical_path_ms": critical_path(t), "ring_ms": ring_time(t, t_comm),
+                     "balanced_ms": mean_path(t),
+                     "round_max_ms": [max(row) for row in t],
+                     "round_max_over_mean": [max(row) / (sum(row) / len(row)) for row in t]}
+    out["speedup_compute_bound"] = out["contiguous"]["critical_path_ms"] / out["striped"]["critical_path_ms"]
+    out["speedup_with_comm"] = out["contiguous"]["ring_ms"] / out["striped"]["ring_ms"]
+    return out
+
+
+def time_device_rounds(q, k, v, n_dev, layout, reps=3):
+    """t[r][d] in ms: one launch per (round, device) on device-layout q, k, v,
+    bracketed by events on the current stream; median over `reps` after one
+    warm-up pass."""
+    import torch
+    import striped_ring_attention_amd as sra
+    B, S, H, D = q.shape
+    o = torch.empty((B, S, H, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, S, H), dtype=torch.float32, device=q.device)
+    samples = [[[] for _ in range(n_dev)] for _ in range(n_dev)]
+    for rep in range(reps + 1):
+        evs = []
+        for r in range(n_dev):
+            for d in range(n_dev):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                sra.ring_round_attn(q, k, v, n_dev, layout, r, device=d, o_part=o, lse_part=lse)
+                b.record()
+                evs.append((r, d, a, b))
+        torch.cuda.synchronize()
+        if rep == 0:
+            continue
+        for r, d, a, b in evs:
+            samples[r][d].append(a.elapsed_time(b))
+    return [[statistics.median(samples[r][d]) for d in range(n_dev)] for r in range(n_dev)]
+
+
+def simulate(workload="long", reps=3, link_gbps=DEFAULT_LINK_GBPS, seed=None):
+    """Times both layouts of a named workload and returns the projection."""
+    import torch
+    import striped_ring_attention_amd as sra
+    from striped_ring_attention_amd.inputs import WORKLOADS, make_inputs
+    sra.load()
+    w = WORKLOADS[workload]
+    over = {} if seed is None else {"seed": seed}
+    x = make_inputs(workload, device="cuda", **over)
+    N = w["n_dev"]
+    q, k, v = x["q"], x["k"], x["v"]
+    t_contig = time_device_rounds(q, k, v, N, sra.CONTIGUOUS, reps)
+    qs, ks, vs = (sra.stripe_permute(t, N) for t in (q, k, v))
+    del q, k, v, x
+    t_striped = time_device_rounds(qs, ks, vs, N, sra.STRIPED, reps)
+    B, S, H, D = qs.shape
+    res = project(t_striped, t_contig, kv_block_bytes(B, S, H, D, N, qs.element_size()), link_gbps)
+    pairs = {name: sra.count_live_pairs(S, N, lay).numpy() for name, lay in
+             (("striped", sra.STRIPED), ("contiguous", sra.CONTIGUOUS))}
+    ideal = {n: float(p.max(axis=1).sum()) for n, p in pairs.items()}
+    res["speedup_ideal_pairs"] = ideal["contiguous"] / ideal["striped"]
+    res["workload"] = {"name": workload, "batch": B, "seq": S, "heads": H, "head_dim": D, "ring_devices": N}
+    res["t_ms"] = {"striped": t_striped, "contiguous": t_contig}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--link-gbps", type=float, default=DEFAULT_LINK_GBPS)
+    args = ap.parse_args()
+    print(json.dumps(simulate(args.workload, args.reps, args.link_gbps)), flush=True)
+
+
+if __name__ == "__main__":
+    main()
