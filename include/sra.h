@@ -176,7 +176,8 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k,
                       size_t workspace_bytes, int64_t* live_counts,
                       void* const* round_events, void* stream);
 
-/* Bytes of workspace sra_ring_attn_bwd needs for desc (fp32 [B, S, H]). */
+/* Bytes of workspace sra_ring_attn_bwd needs for desc: fp32 [B, H, S, 2],
+ * per row the log2-scaled LSE and Delta = rowsum(dout * o). */
 size_t sra_bwd_workspace_bytes(const sra_desc* desc);
 
 /* Gradient of the ring forward: every round for every device, bf16 with

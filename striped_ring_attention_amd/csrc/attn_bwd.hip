@@ -46,22 +46,30 @@ constexpr int KP = D + 8;     // row-major tile pitch in LDS (elements)
 
 // ------------------------------------------------------------------ Delta --
 
-// Sixteen lanes per (b, slot, h) row, each taking 8 consecutive elements
-// (16-byte loads, so a wave reads four whole 256-byte rows of O and of dO),
-// then a 16-lane butterfly sum: Delta = sum_c dO[c] * O[c] in fp32.
+// Row statistics of the backward, one float pair per row in a head-major
+// layout [B, H, S, 2]: (LSE * log2 e, Delta), Delta = sum_c dO[c] * O[c] in
+// fp32. The rows of one head are contiguous, so the 32 rows of a query tile
+// are 256 contiguous bytes. Sixteen lanes per (b, slot, h) row, each taking
+// 8 consecutive elements (16-byte loads: a wave reads four whole 256-byte
+// rows of O and of dO), then a 16-lane butterfly sum.
 __global__ void __launch_bounds__(256) bwd_delta(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                                                 float* __restrict__ delta, uint64_t rows) {
-    const uint64_t stride = ((uint64_t)gridDim.x * blockDim.x) >> 4;
+                                                 const float* __restrict__ lse, float* __restrict__ stats,
+                                                 uint32_t rows, uint32_t S, uint32_t H) {
+    const uint32_t stride = (gridDim.x * blockDim.x) >> 4;
     const int c = threadIdx.x & 15;
-    for (uint64_t r = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4; r < rows; r += stride) {
-        const bf16x8 x = *(const bf16x8*)(o + r * D + 8 * c);
-        const bf16x8 y = *(const bf16x8*)(dout + r * D + 8 * c);
+    for (uint32_t r = (blockIdx.x * blockDim.x + threadIdx.x) >> 4; r < rows; r += stride) {
+        const bf16x8 x = *(const bf16x8*)(o + (uint64_t)r * D + 8 * c);
+        const bf16x8 y = *(const bf16x8*)(dout + (uint64_t)r * D + 8 * c);
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
-        if (c == 0) delta[r] = s;
+        if (c == 0) {
+            const uint32_t h = r % H, bs = r / H, b = bs / S, slot = bs % S;
+            const uint64_t i = ((uint64_t)b * H + h) * S + slot;
+            *(float2*)(stats + 2 * i) = float2{lse[r] * kLog2e, s};
+        }
     }
 }
 
@@ -123,8 +131,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
             doreg[kk] = dp[2 * kk];
         }
     }
-    const float lse_l2 = row_ok ? a.lse[row] * kLog2e : 0.f;
-    const float dlt = row_ok ? a.delta[row] : 0.f;
+    const int64_t srow = (wi.b * a.H + wi.h) * a.S + (int64_t)d * a.L + min(j, L - 1);
+    const float2 st2 = *(const float2*)(a.stats + 2 * srow);
+    const float lse_l2 = row_ok ? st2.x : 0.f;
+    const float dlt = row_ok ? st2.y : 0.f;
     __builtin_amdgcn_s_waitcnt(0);   // row operands land before any tile load is issued
 
     f32x16 dqacc[4];
@@ -247,19 +257,34 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
 
 // ----------------------------------------------------------------- dK/dV --
 
-constexpr int KBM = 128;          // keys per workgroup
+constexpr int KBM = 128;          // keys per workgroup (4 waves x 32)
 constexpr int KBQ = 32;           // query rows per tile
-constexpr int QTP = KBQ + 8;      // Q^T / dO^T tile pitch (elements)
+constexpr int DK_NS = 4;          // LDS stages
+constexpr int DK_AHEAD = 3;       // tiles in flight ahead of the one computed
+constexpr int kWaitVm10 = 0x0F7A; // vmcnt(10): the two newest tiles (5 loads each per wave) may be in flight
+
+// Q and dO tiles are stored row-major with 256-byte rows and no padding
+// (they are loaded straight into LDS); 16-byte chunk c of row r sits in slot
+// c ^ swz(r), swz(r) = 4 (r % 4) + (r / 4) % 4. This one swizzle keeps both
+// read patterns conflict-free: 16 lanes reading one chunk of 16 consecutive
+// rows (the MFMA row operand) hit 16 different slots, and a transposing read
+// (4 consecutive rows x 4 consecutive chunks per 32 lanes) hits 16 as well.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 struct __align__(16) SmemDkdv {
-    bf16 qr[KBQ * KP];    // Q tile, row-major
-    bf16 dor[KBQ * KP];   // dO tile, row-major
-    bf16 qt[D * QTP];     // Q tile, dimension-major, permuted query order
-    bf16 dot[D * QTP];    // dO tile, dimension-major, permuted query order
-    float lse[KBQ];       // log2-scaled LSE of the tile's rows
-    float dl[KBQ];        // Delta of the tile's rows
+    bf16 q[DK_NS][KBQ * D];       // Q tiles
+    bf16 dout[DK_NS][KBQ * D];    // dO tiles
+    float st[DK_NS][4][64];       // row statistics (LSE log2 e, Delta) of the tile's 32 rows; one copy per wave
 };
 
+// A workgroup owns 128 keys (4 waves x 32) of one source device and walks,
+// round by round, the 32-row query tiles of the device that meets the block
+// in that round (from the first tile with a live pair). Per tile:
+// S = Q K^T and dP = dO V^T on MFMA (Q and dO rows from LDS, K and V held in
+// registers), P = 2^(S scale log2 e - LSE log2 e), dS = P (dP - Delta) scale,
+// then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read from the same
+// row-major tiles through ds_read_b64_tr_b16. Tiles stream into a 4-stage
+// LDS ring three tiles ahead; one barrier per tile.
 __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     __shared__ SmemDkdv sm;
     const int L = (int)a.L;
@@ -268,13 +293,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     const int s = (int)wi.d;                               // the key block's owner
     const int ktile = (int)wi.heavy_rank;                  // early keys meet the most queries
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
     const int k0 = ktile * KBM;
 
     const int rs = (int)(a.H * D);
     const int row_bytes = rs * 2;
     const uint64_t q_head = uniform_u64((uint64_t)((const bf16*)a.q + (wi.b * a.S * a.H + wi.h) * D));
     const uint64_t do_head = uniform_u64((uint64_t)((const bf16*)a.dout + (wi.b * a.S * a.H + wi.h) * D));
+    const uint64_t st_head = uniform_u64((uint64_t)(a.stats + 2 * (wi.b * a.H + wi.h) * a.S));
     const uint64_t slab_stride = (uint64_t)a.L * (uint64_t)row_bytes;
     const int slab_bytes = __builtin_amdgcn_readfirstlane((L - 1) * row_bytes + D * 2);
     const int nqt = (L + KBQ - 1) / KBQ;
@@ -282,7 +308,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     // Rounds: in round r the block of device s meets the queries of device
     // (s + r) mod N. Query rows that see any key of this workgroup start at
     // k0 - delta + 1 (the live keys of row j are those < j + delta).
-    auto qdev = [&](int r) { return (s + r) % a.N; };
+    auto qdev = [&](int r) {
+        const int x = s + r;
+        return x >= a.N ? x - a.N : x;
+    };
     auto delta_of = [&](int r) { return clamp_delta(live_delta(a.layout, a.N, L, qdev(r), s), L); };
     auto first_tile = [&](int r) { return min(max(k0 - delta_of(r) + 1, 0), L) / KBQ; };
     int n_tiles = 0;
@@ -317,47 +346,47 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     const float sl = a.scale_log2;
     const float scale = a.scale;
 
-    // Tile staging: threads 0-127 stage Q, 128-255 stage dO, as (query quad
-    // qq, 8-dim chunk dc): four rows x 16 bytes, written row-major and
-    // transposed. Threads 0-31 / 32-63 also fetch the tile's LSE / Delta.
-    const int half = tid >> 7, lt = tid & 127;
-    const int qq = lt & 7, dc = lt >> 3;
-    const int st_voff = 4 * qq * row_bytes + dc * 16;
-    const uint64_t st_head = uniform_u64(half == 0 ? q_head : do_head);   // wave-uniform
-    const int qt_col = 16 * (qq >> 2) + 4 * ((qq & 1) * 2 + ((qq >> 1) & 1));
-    u32x4 st[4];
-    float sc_val = 0.f;
-
-    auto load_tile = [&](int r, int tq, bool valid) {
+    // Loads: wave w issues instructions w and w + 4 of each 8-instruction
+    // (8 KiB) tile of Q and of dO, instruction i covering rows 4i .. 4i+3;
+    // lane l writes row 4i + l/16, slot l % 16, loading the chunk that slot
+    // holds (for these rows swz = 4 (l/16) + w). Each wave also loads the
+    // tile's 64 statistics floats into its own copy.
+    const int ld_voff = (4 * w + (lane >> 4)) * row_bytes + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | w));
+    const int ld_step = 16 * row_bytes;
+    auto load_tile = [&](int r, int tq, bool valid, int stage) {
         const int dq = qdev(r);
         const int tile_off = tq * KBQ * row_bytes;
         int left = slab_bytes - tile_off;
         left = (valid && left > 0) ? left : 0;
-        const __amdgpu_buffer_rsrc_t rsrc =
-            slab_rsrc((const void*)(st_head + (uint64_t)dq * slab_stride + (uint64_t)tile_off), left);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, st_voff + i * row_bytes, 0, 0);
-        if (tid < 64) {
-            const int jr = tq * KBQ + (tid & 31);
-            const int64_t srow = (wi.b * a.S + (int64_t)dq * a.L + min(jr, L - 1)) * a.H + wi.h;
-            sc_val = (valid && jr < L) ? (tid < 32 ? a.lse[srow] * kLog2e : a.delta[srow]) : 0.f;
-        }
+        const uint64_t off = (uint64_t)dq * slab_stride + (uint64_t)tile_off;
+        const i32x4 rq = raw_rsrc(q_head + off, left);
+        const i32x4 rd = raw_rsrc(do_head + off, left);
+        const int srow0 = dq * L + tq * KBQ;                  // first row of the tile within the head
+        const int st_left = valid ? min(256, (a.N * L - srow0) * 8) : 0;
+        const i32x4 rst = raw_rsrc(st_head + (uint64_t)srow0 * 8, st_left);
+        const uint32_t dsq = lds_addr(&sm.q[stage][512 * w]);
+        const uint32_t dsd = lds_addr(&sm.dout[stage][512 * w]);
+        load_lds_b128(rq, ld_voff, dsq);
+        load_lds_b128(rq, ld_voff + ld_step, dsq + 4096);
+        load_lds_b128(rd, ld_voff, dsd);
+        load_lds_b128(rd, ld_voff + ld_step, dsd + 4096);
+        load_lds_b32(rst, 4 * lane, lds_addr(&sm.st[stage][w][0]));
     };
-    auto store_tile = [&]() {
-        bf16* rm = half == 0 ? sm.qr : sm.dor;
-        bf16* tr = half == 0 ? sm.qt : sm.dot;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)&rm[(4 * qq + i) * KP + 8 * dc] = st[i];
-        bf16* td = &tr[(8 * dc) * QTP + qt_col];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint2 lo = {pack_lo(st[0][p], st[1][p]), pack_lo(st[2][p], st[3][p])};
-            uint2 hi = {pack_hi(st[0][p], st[1][p]), pack_hi(st[2][p], st[3][p])};
-            *(uint2*)(td + (2 * p) * QTP) = lo;
-            *(uint2*)(td + (2 * p + 1) * QTP) = hi;
-        }
-        if (tid < 32) sm.lse[tid] = sc_val;
-        else if (tid < 64) sm.dl[tid - 32] = sc_val;
+
+    // Transposing-read addressing (lane (g, j) names key row 16 kk2 + 8 rd +
+    // 4 (g / 2) + j / 4, dims 32 db + 16 (g % 2) + 4 (j % 4) .. +3).
+    const int tg = lane >> 4, tj = lane & 15;
+    const int tr_row = 4 * (tg >> 1) + (tj >> 2);
+    const int tr_c = 2 * (tg & 1) + ((tj & 3) >> 1);      // chunk within the 4-chunk group of a dim block
+    auto tr_ptr = [&](const bf16* tile, int kk2, int rd, int db) {
+        const int row = 16 * kk2 + 8 * rd + tr_row;
+        const int slot = (4 * db + tr_c) ^ swz(row);
+        return tile + row * D + 8 * slot + 4 * (tj & 1);
+    };
+    auto read_t = [&](const bf16* tile, int kk2, int db) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(tr_ptr(tile, kk2, 0, db)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(tr_ptr(tile, kk2, 1, db)));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
     int cr = 0, cq = first_tile(0);
@@ -370,30 +399,43 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     settle(cr, cq);
     int lr = cr, lq = cq;
 
-    if (n_tiles > 0) load_tile(lr, lq, true);
-    for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
+    // Zero LDS once (rows past a slab end are never loaded), then tiles 0..2.
+    {
+        u32x4* z = (u32x4*)&sm;
+        for (int i = tid; i < (int)(sizeof(SmemDkdv) / 16); i += 256) z[i] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bar();
+    }
+#pragma unroll
+    for (int u = 0; u < DK_AHEAD; ++u) {
+        load_tile(lr, lq, u < n_tiles, u);
         ++lq;
         settle(lr, lq);
-        load_tile(lr, lq, t + 1 < n_tiles);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm10);   // tile 0 is in
+    bar();
 
+    for (int t = 0; t < n_tiles; ++t) {
+        load_tile(lr, lq, t + DK_AHEAD < n_tiles, (t + DK_AHEAD) & (DK_NS - 1));
+        ++lq;
+        settle(lr, lq);
+
+        const int stg = t & (DK_NS - 1);
+        const bf16* qs = sm.q[stg];
+        const bf16* ds = sm.dout[stg];
         const int delta = delta_of(cr);
         const int jq0 = cq * KBQ;
         const int jq_last = min(jq0 + KBQ - 1, L - 1);
         // Live pairs for this wave: its first key is live for the tile's last row.
         if (wave_live && kw0 < live32(jq_last, delta, L)) {
-            f32x16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.qr[c32 * KP + 8 * h2], kreg[0],
-                                                                  f32x16{}, 0, 0, 0);
-            f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.dor[c32 * KP + 8 * h2], vreg[0],
-                                                                f32x16{}, 0, 0, 0);
+            f32x16 sacc, dp;
 #pragma unroll
-            for (int kk = 1; kk < 8; ++kk) {
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.qr[c32 * KP + 16 * kk + 8 * h2],
-                                                               kreg[kk], sacc, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.dor[c32 * KP + 16 * kk + 8 * h2],
-                                                             vreg[kk], dp, 0, 0, 0);
+            for (int kk = 0; kk < 8; ++kk) {
+                const int slot = (2 * kk + h2) ^ swz(c32);
+                const bf16x8 qf = *(const bf16x8*)&qs[c32 * D + 8 * slot];
+                const bf16x8 df = *(const bf16x8*)&ds[c32 * D + 8 * slot];
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kreg[kk], kk == 0 ? f32x16{} : sacc, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df, vreg[kk], kk == 0 ? f32x16{} : dp, 0, 0, 0);
             }
             // Accumulator element i of this lane is query jq0 + 8*(i/4) + 4*h2 + i%4
             // against key kw. The tile is fully live when all its rows are in
@@ -407,31 +449,38 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
                 }
             }
             bf16x8 pb[2], dsb[2];
+            const float* stt = sm.st[stg][0];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 l4 = *(const f32x4*)&sm.lse[8 * g + 4 * h2];
-                const f32x4 d4 = *(const f32x4*)&sm.dl[8 * g + 4 * h2];
+                // (LSE log2 e, Delta) of rows 8g + 4h2 .. +3
+                const f32x4 s01 = *(const f32x4*)&stt[2 * (8 * g + 4 * h2)];
+                const f32x4 s23 = *(const f32x4*)&stt[2 * (8 * g + 4 * h2) + 4];
+                const float lz[4] = {s01[0], s01[2], s23[0], s23[2]};
+                const float dz[4] = {s01[1], s01[3], s23[1], s23[3]};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * g + e;
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl, -l4[e]));
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl, -lz[e]));
                     pb[i >> 3][i & 7] = (bf16)p;
-                    dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - d4[e]) * scale);
+                    dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dz[e]) * scale);
                 }
             }
 #pragma unroll
             for (int kk2 = 0; kk2 < 2; ++kk2) {
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    const int off = (db * 32 + c32) * QTP + 16 * kk2 + 8 * h2;
-                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.dot[off], pb[kk2], dvacc[db], 0, 0, 0);
-                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)&sm.qt[off], dsb[kk2], dkacc[db], 0, 0, 0);
+                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_t(ds, kk2, db), pb[kk2], dvacc[db], 0, 0, 0);
+                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_t(qs, kk2, db), dsb[kk2], dkacc[db], 0, 0, 0);
                 }
             }
         }
         ++cq;
         settle(cr, cq);
+        __builtin_amdgcn_s_waitcnt(kWaitVm10);   // tile t+1 is in
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bar();
     }
+    __builtin_amdgcn_s_waitcnt(0);   // no load may still be writing LDS when the workgroup ends
 
     if (!key_ok) return;
     bf16* dkp = (bf16*)a.dk + krow * D;
@@ -458,7 +507,7 @@ hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream) {
     if (blocks > 256ull * 64) blocks = 256ull * 64;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(bwd_delta, dim3((unsigned)blocks), dim3(256), 0, stream, (const bf16*)a.o, (const bf16*)a.dout,
-                       a.delta, rows);
+                       a.lse, a.stats, (uint32_t)rows, (uint32_t)a.S, (uint32_t)a.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nq = (a.L + QBM - 1) / QBM * a.H * a.N * a.B;

@@ -96,42 +96,8 @@ struct __align__(16) SmemBf16 {
     bf16 v[NS][BN * D];
 };
 
-// Workgroup barrier without a memory fence. The K/V loads write LDS
-// asynchronously; a fenced barrier would make every wave wait for all of its
-// loads in flight, which is exactly what the deep prefetch avoids. Ordering
-// is explicit instead: a loading wave waits for its own loads of a tile
-// (vmcnt) before the barrier that precedes the tile's first read, and LDS
-// reads are complete (lgkmcnt) before the barriers after which their buffer
-// can be refilled.
-__device__ __forceinline__ void bar() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
-// expcnt in 6:4, lgkmcnt in 11:8; a field at its maximum is not waited on.
-constexpr int kWaitLgkm0 = 0xC07F;                // lgkmcnt(0)
-constexpr int kWaitVm4 = 0x0F74;                  // vmcnt(4)
-constexpr int kWaitVm8 = 0x0F78;                  // vmcnt(8)
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// One buffer_load_dwordx4 ... lds: lane l's 16 bytes at buffer offset voff go
-// to LDS byte lds + 16 l (LDS base in M0). Issued from inline assembly so that
-// the compiler's wait insertion, which would otherwise make every later LDS
-// read wait for all loads in flight, leaves the loads alone; their
-// completion is awaited explicitly (vmcnt) before the barrier that publishes
-// the tile.
-__device__ __forceinline__ void load_lds_b128(i32x4 rsrc, int voff, uint32_t lds) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-#define SRA_LDS4(p) ((__attribute__((address_space(3))) s16x4*)(p))
+constexpr int kWaitVm4 = 0x0F74;   // vmcnt(4)
+constexpr int kWaitVm8 = 0x0F78;   // vmcnt(8)
 
 // Walks the (round, key tile) pairs one workgroup visits, in ring order:
 // rounds r_lo .. r_hi-1, and within a round the key tiles of the source
@@ -264,7 +230,7 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
         int left = slab_bytes - tile_off;
         left = (valid && left > 0) ? left : 0;
         const uint64_t base = ld_head + (uint64_t)c.s * slab_stride + (uint64_t)tile_off;
-        const i32x4 rsrc = {(int)(uint32_t)base, (int)(uint32_t)(base >> 32) & 0xFFFF, left, kBufferFlags};
+        const i32x4 rsrc = raw_rsrc(base, left);
         const uint32_t dst = lds_addr(ld_lds0 + stage * (BN * D));
 #pragma unroll
         for (int q = 0; q < 4; ++q) load_lds_b128(rsrc, ld_voff + q * ld_step, dst + 4096 * q);

@@ -51,6 +51,66 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
 }
 
+// ------------------------------------------------- loads straight into LDS --
+
+// Workgroup barrier without a memory fence. Loads that write LDS directly
+// complete asynchronously; a fenced barrier would make every wave wait for
+// all of its loads in flight, which is exactly what a deep prefetch avoids.
+// Ordering is explicit instead: a loading wave waits for its own loads of a
+// tile (vmcnt) before the barrier that precedes the tile's first read, and
+// LDS reads are complete (lgkmcnt) before the barriers after which their
+// buffer can be refilled.
+__device__ __forceinline__ void bar() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits 3:0 and 15:14,
+// expcnt in 6:4, lgkmcnt in 11:8; a field at its maximum is not waited on.
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0)
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for `bytes` bytes at `base` (raw buffer: offsets at or
+// past `bytes` read as zero), as four scalar words. Both arguments must be
+// wave-uniform; readfirstlane keeps them in scalar registers even where the
+// compiler cannot prove it.
+__device__ __forceinline__ i32x4 raw_rsrc(uint64_t base, int bytes) {
+    const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    const int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)) & 0xFFFF;
+    return i32x4{lo, hi, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags};
+}
+
+// One buffer_load_dwordx4 ... lds: lane l's 16 bytes at buffer offset voff go
+// to LDS byte lds + 16 l (LDS base in M0). Issued from inline assembly so that
+// the compiler's wait insertion, which would otherwise make every later LDS
+// read wait for all loads in flight, leaves the loads alone; their
+// completion is awaited explicitly (vmcnt) before the barrier that publishes
+// the tile.
+__device__ __forceinline__ void load_lds_b128(i32x4 rsrc, int voff, uint32_t lds) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+// The same with 4 bytes per lane (LDS byte lds + 4 l).
+__device__ __forceinline__ void load_lds_b32(i32x4 rsrc, int voff, uint32_t lds) {
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define SRA_LDS4(p) ((__attribute__((address_space(3))) s16x4*)(p))
+
+// ds_read_b64_tr_b16 pair: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte pieces named by lanes 4v + i / 4 (v = 0..3);
+// `p` and `p + row8` name two pieces, giving 8 values per lane.
+__device__ __forceinline__ bf16x8 read_tr8(const bf16* p, int row8) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(p + row8));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <bool B>
 struct BoolTag {
     static constexpr bool value = B;

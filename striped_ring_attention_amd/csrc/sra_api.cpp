@@ -323,7 +323,7 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k, const 
 
 size_t sra_bwd_workspace_bytes(const sra_desc* desc) {
     if (check_desc(desc)) return 0;
-    return (size_t)(desc->batch * desc->seq * desc->heads) * sizeof(float);
+    return (size_t)(desc->batch * desc->seq * desc->heads) * 2 * sizeof(float);
 }
 
 int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const void* v, const void* o,
@@ -333,6 +333,8 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
     if (st) return st;
     if (desc->dtype != SRA_DTYPE_BF16)
         return fail(SRA_ERR_UNSUPPORTED, "the backward is built for bf16 with head_dim 128 only");
+    if ((uint64_t)(desc->batch * desc->seq * desc->heads) >= (1ull << 32))
+        return fail(SRA_ERR_UNSUPPORTED, "the backward indexes rows with 32 bits: batch * seq * heads < 2^32");
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
         return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
     for (const void* p : std::initializer_list<const void*>{q, k, v, o, dout, dq, dk, dv})
@@ -360,7 +362,7 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
     a.o = o;
     a.lse = lse;
     a.dout = dout;
-    a.delta = (float*)workspace;
+    a.stats = (float*)workspace;
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;

@@ -61,7 +61,7 @@ struct BwdArgs {
     const void* o;
     const float* lse;     // fp32 [B,S,H], natural log
     const void* dout;
-    float* delta;         // fp32 [B,S,H] workspace: rowsum(dO * O)
+    float* stats;         // fp32 [B,H,S,2] workspace: per row (LSE * log2 e, rowsum(dO * O))
     void* dq;
     void* dk;
     void* dv;
