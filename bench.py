@@ -1,12 +1,17 @@
 """Benchmark: striped ring-attention forward on one MI355X.
 
-One step = stripe-permute Q, K, V (original order -> striped device layout)
--> all N ring rounds -> unstripe O and LSE. Inputs are resident in HBM before
-the timed region. The ring runs with the fused schedule by default (one
-launch walks every (round, key tile) pair, the log-sum-exp merge done
-online); the per-round schedule (one launch per ring round, merge fused in
-its epilogue) is timed alongside, as is the contiguous layout. Prints one
-JSON line.
+One step = original-order Q, K, V -> striped device layout -> all N ring
+rounds -> O and LSE back in original order. By default (--order original)
+that is one launch: the ring kernel addresses device d's j-th token at its
+position j*N + d, so the stripe permutation and its inverse are folded into
+its row addressing. With --order device the step runs the explicit gather
+kernels (stripe_permute Q, K, V; ring on device-layout tensors; unstripe O
+and LSE); that variant is timed alongside either way. Inputs are resident in
+HBM before the timed region. The ring runs with the fused schedule by
+default (one launch walks every (round, key tile) pair, the log-sum-exp
+merge done online); the per-round schedule (one launch per ring round, merge
+fused in its epilogue) and the contiguous layout are timed alongside. Prints
+one JSON line.
 
 value  = useful causal TFLOP/s of the whole step: 4*Dh flops per live causal
          pair, B*H*S*(S+1)/2 pairs per step (masked pairs inside partial
@@ -54,6 +59,10 @@ def parse():
     ap.add_argument("--layout", default="striped", choices=["striped", "contiguous"])
     ap.add_argument("--schedule", default="fused", choices=["fused", "per_round"],
                     help="ring schedule of the timed step (the other one is timed alongside)")
+    ap.add_argument("--order", default="original", choices=["original", "device"],
+                    help="original: q, k, v, o, lse in token order, the stripe permutation folded into the ring "
+                         "kernel's row addressing (one launch per step); device: gather into the striped "
+                         "device layout, ring, gather back (the other one is timed alongside)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-compare", action="store_true", help="skip the other-schedule and contiguous runs")
@@ -124,13 +133,13 @@ def traffic_detail(workload, sched, layout):
     return {k: TRAFFIC[k] for k in ("fetch_bytes_per_launch", "write_bytes_per_launch", "copy_scale")}
 
 
-def time_backward(sra, torch, x, N, layout, fwd_step, qd, kd, vd, o_dev, lse_dev, o, lse, K, useful_fwd_flops):
+def time_backward(sra, torch, x, N, layout, ordr, fwd_step, qd, kd, vd, o_dev, lse_dev, o, lse, K, useful_fwd_flops):
     """The ring backward (dQ, dK, dV) on the forward's device-layout outputs:
     K launches of the three backward kernels, each bracketed by events on the
     current stream. Useful flops: 10*Dh per live causal pair (S recomputed,
     dP, dV, dQ, dK), i.e. 2.5x the forward's."""
     fwd_step()
-    if layout == sra.STRIPED:
+    if layout == sra.STRIPED and ordr == sra.ORDER_DEVICE:
         q, k, v, out, l = qd, kd, vd, o_dev, lse_dev
         do = sra.stripe_permute(x["do"], N)
     else:
@@ -138,12 +147,12 @@ def time_backward(sra, torch, x, N, layout, fwd_step, qd, kd, vd, o_dev, lse_dev
     dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
     ws = torch.empty(max(1, sra.bwd_workspace_bytes(q, N, layout)), dtype=torch.uint8, device=q.device)
     for _ in range(2):
-        sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
+        sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws, order=ordr)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     for a, b in evs:
         a.record()
-        sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws)
+        sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws, order=ordr)
         b.record()
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in evs) / K
@@ -191,11 +200,17 @@ def main():
     def launches(sc):
         return N if sc == sra.SCHEDULE_PER_ROUND else 1
 
-    def step(lay, sc, events=None, perm_events=None, cnt=None):
+    ordr = sra.ORDER_ORIGINAL if args.order == "original" else sra.ORDER_DEVICE
+
+    def step(lay, sc, events=None, perm_events=None, cnt=None, od=None):
+        od = ordr if od is None else od
+
         def ring(a, b, c, out, l_out):
             sra.ring_attn_fwd(a, b, c, N, lay, schedule=sc, out=out, lse=l_out, workspace=ws, live_counts=cnt,
-                              round_events=events)
-        if lay == sra.STRIPED:
+                              round_events=events, order=od)
+        if od == sra.ORDER_ORIGINAL:
+            ring(q, k, v, o, lse)
+        elif lay == sra.STRIPED:
             if perm_events:
                 perm_events[0].record()
             for src, dst in ((q, qd), (k, kd), (v, vd)):
@@ -218,7 +233,7 @@ def main():
             e.record()          # create the underlying HIP event before its handle is passed on
         return evs
 
-    def timed(lay, sc, K, perm=False):
+    def timed(lay, sc, K, perm=False, od=None):
         """K steps; returns (ms per step, kernel ms per launch list per step, permutation events)."""
         nl = launches(sc)
         evs = [new_events(2 * nl) for _ in range(K)]
@@ -227,7 +242,7 @@ def main():
         torch.cuda.synchronize()
         t0.record()
         for i in range(K):
-            step(lay, sc, events=[e.cuda_event for e in evs[i]], perm_events=pev[i])
+            step(lay, sc, events=[e.cuda_event for e in evs[i]], perm_events=pev[i], od=od)
         t1.record()
         torch.cuda.synchronize()
         per_launch = [[evs[i][2 * r].elapsed_time(evs[i][2 * r + 1]) for r in range(nl)] for i in range(K)]
@@ -241,7 +256,8 @@ def main():
 
     K = args.steps
     wall0 = time.perf_counter()
-    ms_step, per_launch, perm_ev = timed(layout, sched, K, perm=(layout == sra.STRIPED))
+    dev_striped = ordr == sra.ORDER_DEVICE and layout == sra.STRIPED
+    ms_step, per_launch, perm_ev = timed(layout, sched, K, perm=dev_striped)
     wall = time.perf_counter() - wall0
     attn_ms = sum(sum(p) for p in per_launch) / K
     nl = launches(sched)
@@ -254,7 +270,16 @@ def main():
     else:
         flops_per_launch = [useful_flops]
 
+    # The explicit gather kernels (device order, striped): the timed step itself
+    # when --order device, else a run of its own.
     perm = {}
+    dev_step = None
+    if layout == sra.STRIPED and not dev_striped:
+        step(layout, sched, od=sra.ORDER_DEVICE)
+        d_step, d_launch, perm_ev = timed(layout, sched, K, perm=True, od=sra.ORDER_DEVICE)
+        d_attn = sum(sum(p) for p in d_launch) / K
+        dev_step = {"step_ms": d_step, "step_useful_TFLOPs": useful_flops / (d_step * 1e-3) / 1e12,
+                    "ring_ms": d_attn, "ring_useful_TFLOPs": useful_flops / (d_attn * 1e-3) / 1e12}
     if layout == sra.STRIPED:
         p_ms = sum(perm_ev[i][0].elapsed_time(perm_ev[i][1]) for i in range(K)) / K
         u_ms = sum(perm_ev[i][2].elapsed_time(perm_ev[i][3]) for i in range(K)) / K
@@ -301,6 +326,8 @@ def main():
             compare[cname] = rec
         compare[f"{args.layout}_{args.schedule}"] = {"ring_ms": attn_ms, "ring_useful_TFLOPs": attn_tflops,
                                                      "step_ms": ms_step}
+        if dev_step is not None:
+            compare[f"{args.layout}_{args.schedule}_device_order"] = dev_step
 
     critical = None
     if not args.no_critical_path:
@@ -315,15 +342,16 @@ def main():
 
     backward = None
     if not args.no_backward:
-        backward = time_backward(sra, torch, x, N, layout, lambda: step(layout, sched), qd, kd, vd, o_dev, lse_dev,
-                                 o, lse, K, useful_flops)
+        backward = time_backward(sra, torch, x, N, layout, ordr, lambda: step(layout, sched), qd, kd, vd, o_dev,
+                                 lse_dev, o, lse, K, useful_flops)
 
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "seq_len": S, "heads": H, "head_dim": D,
-                   "ring_devices": N, "layout": args.layout, "schedule": args.schedule, "causal": True,
+                   "ring_devices": N, "layout": args.layout, "schedule": args.schedule, "order": args.order,
+                   "causal": True,
                    "pass": "forward"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -24,6 +24,12 @@
  * sra_stripe_permute converts original order to striped device layout once,
  * before the ring (the pages apply the permutation once, before the first
  * layer; "Key points: Striped layout"), and sra_unstripe converts back.
+ * With desc->order = SRA_ORDER_ORIGINAL the ring entry points instead take
+ * and return tensors in original token order and address device d's j-th
+ * token at its position directly (row j*N + d when striped): the
+ * permutation is folded into the kernels' row addressing and no permuted
+ * copy exists. Results are bit-identical to the device-layout call followed
+ * by sra_unstripe.
  *
  * Causality: key slot k of device s is live for query slot j of device d
  * when position(s, k) <= position(d, j) (diagonal included). Scores are
@@ -52,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SRA_ABI_VERSION 1
+#define SRA_ABI_VERSION 2
 
 enum sra_status {
     SRA_OK = 0,
@@ -64,6 +70,10 @@ enum sra_status {
 
 enum sra_layout { SRA_LAYOUT_CONTIGUOUS = 0, SRA_LAYOUT_STRIPED = 1 };
 enum sra_dtype { SRA_DTYPE_F32 = 0, SRA_DTYPE_BF16 = 1 };
+enum sra_order {
+    SRA_ORDER_DEVICE = 0,   /* tensors in device layout (slot d*L + j) */
+    SRA_ORDER_ORIGINAL = 1  /* tensors in original token order (slot = position) */
+};
 enum sra_schedule {
     SRA_SCHEDULE_PER_ROUND = 0, /* one kernel launch per ring round, LSE merge fused in its epilogue */
     SRA_SCHEDULE_FUSED = 1      /* all rounds in one launch, merged online (no partial traffic) */
@@ -82,6 +92,7 @@ typedef struct sra_desc {
     int32_t dtype;     /* enum sra_dtype: element type of q, k, v and o */
     int32_t schedule;  /* enum sra_schedule (sra_ring_attn_fwd only) */
     float scale;       /* softmax scale; 0 selects 1/sqrt(head_dim) */
+    int32_t order;     /* enum sra_order: how q, k, v, o, lse (and gradients) are ordered */
 } sra_desc;
 
 /* Library ABI version (SRA_ABI_VERSION of the build). */

@@ -24,6 +24,8 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 SCHEDULE_PER_ROUND = 0
 SCHEDULE_FUSED = 1
+ORDER_DEVICE = 0     # tensors in device layout (slot d*L + j)
+ORDER_ORIGINAL = 1   # tensors in original token order; the kernels address device rows in place
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsra.so")
 
@@ -36,7 +38,7 @@ class SraDesc(ctypes.Structure):
     _fields_ = [
         ("batch", _i64), ("seq", _i64), ("heads", _i64), ("head_dim", _i64),
         ("n_dev", _i32), ("layout", _i32), ("dtype", _i32), ("schedule", _i32),
-        ("scale", _f32),
+        ("scale", _f32), ("order", _i32),
     ]
 
 
@@ -110,17 +112,18 @@ def _dtype_code(dt):
     raise ValueError(f"unsupported dtype {dt}")
 
 
-def make_desc(batch, seq, heads, head_dim, n_dev, layout, dtype=DTYPE_BF16, scale=0.0, schedule=SCHEDULE_PER_ROUND):
+def make_desc(batch, seq, heads, head_dim, n_dev, layout, dtype=DTYPE_BF16, scale=0.0, schedule=SCHEDULE_PER_ROUND,
+              order=ORDER_DEVICE):
     if isinstance(dtype, torch.dtype):
         dtype = _dtype_code(dtype)
-    return SraDesc(batch, seq, heads, head_dim, n_dev, layout, dtype, schedule, scale)
+    return SraDesc(batch, seq, heads, head_dim, n_dev, layout, dtype, schedule, scale, order)
 
 
-def _desc_for(q, n_dev, layout, scale, schedule=SCHEDULE_PER_ROUND):
+def _desc_for(q, n_dev, layout, scale, schedule=SCHEDULE_PER_ROUND, order=ORDER_DEVICE):
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, S, H, Dh]")
     B, S, H, D = q.shape
-    return make_desc(B, S, H, D, n_dev, layout, _dtype_code(q.dtype), scale, schedule)
+    return make_desc(B, S, H, D, n_dev, layout, _dtype_code(q.dtype), scale, schedule, order)
 
 
 def _check_tensors(*ts):
@@ -203,10 +206,10 @@ def unstripe(y, n_dev, out=None):
 
 
 def ring_round_attn(q, k, v, n_dev, layout, round, device=-1, scale=0.0, o_part=None, lse_part=None,
-                    live_counts=None):
+                    live_counts=None, order=ORDER_DEVICE):
     """One ring round: partial (O fp32, LSE fp32) for the selected device(s)."""
     _check_tensors(q, k, v, o_part, lse_part, live_counts)
-    d = _desc_for(q, n_dev, layout, scale)
+    d = _desc_for(q, n_dev, layout, scale, order=order)
     B, S, H, D = q.shape
     if o_part is None:
         o_part = torch.zeros((B, S, H, D), dtype=torch.float32, device=q.device)
@@ -227,10 +230,11 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part):
 
 
 def ring_attn_fwd(q, k, v, n_dev, layout, scale=0.0, schedule=SCHEDULE_PER_ROUND, out=None, lse=None,
-                  workspace=None, live_counts=None, round_events=None):
-    """All N rounds of the ring on device-layout q, k, v; returns (O, LSE) in device layout."""
+                  workspace=None, live_counts=None, round_events=None, order=ORDER_DEVICE):
+    """All N rounds of the ring; returns (O, LSE) in the order of q, k, v
+    (device layout, or original token order with order=ORDER_ORIGINAL)."""
     _check_tensors(q, k, v, out, lse, workspace, live_counts)
-    d = _desc_for(q, n_dev, layout, scale, schedule)
+    d = _desc_for(q, n_dev, layout, scale, schedule, order)
     B, S, H, D = q.shape
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, S, H), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -247,10 +251,11 @@ def ring_attn_fwd(q, k, v, n_dev, layout, scale=0.0, schedule=SCHEDULE_PER_ROUND
     return out, lse
 
 
-def ring_attn_bwd(q, k, v, o, lse, dout, n_dev, layout, scale=0.0, dq=None, dk=None, dv=None, workspace=None):
+def ring_attn_bwd(q, k, v, o, lse, dout, n_dev, layout, scale=0.0, dq=None, dk=None, dv=None, workspace=None,
+                  order=ORDER_DEVICE):
     """Gradient of the ring forward on device-layout tensors; returns (dq, dk, dv)."""
     _check_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
-    d = _desc_for(q, n_dev, layout, scale)
+    d = _desc_for(q, n_dev, layout, scale, order=order)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -263,10 +268,12 @@ def ring_attn_bwd(q, k, v, o, lse, dout, n_dev, layout, scale=0.0, dq=None, dk=N
     return dq, dk, dv
 
 
-def striped_attention(q, k, v, n_dev, scale=0.0, schedule=SCHEDULE_PER_ROUND):
-    """Original-order q, k, v -> stripe -> ring over all rounds -> unstripe.
+def striped_attention(q, k, v, n_dev, scale=0.0, schedule=None):
+    """Original-order q, k, v -> striped ring over all rounds, the stripe
+    permutation folded into the kernels' row addressing. The schedule
+    defaults to the fused one for bf16 and per-round for fp32.
 
     Returns (O, LSE) in original order: exact causal attention."""
-    qs, ks, vs = (stripe_permute(t, n_dev) for t in (q, k, v))
-    o, lse = ring_attn_fwd(qs, ks, vs, n_dev, STRIPED, scale, schedule)
-    return unstripe(o, n_dev), unstripe(lse, n_dev)
+    if schedule is None:
+        schedule = SCHEDULE_FUSED if q.dtype == torch.bfloat16 else SCHEDULE_PER_ROUND
+    return ring_attn_fwd(q, k, v, n_dev, STRIPED, scale, schedule, order=ORDER_ORIGINAL)

@@ -99,11 +99,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
 
     const int rs = (int)(a.H * D);
     const int row_bytes = rs * 2;
-    const int64_t slot0 = wi.b * a.S + (int64_t)d * a.L;   // first slot of device d
+    // Device t's j-th token sits at slot mem_slot(t, j); consecutive tokens of
+    // a device are rstride bytes apart.
+    const bool strided = a.strided != 0;
+    const int rstride = (int)(strided ? a.N : 1) * row_bytes;
     const uint64_t k_head = uniform_u64((uint64_t)((const bf16*)a.k + (wi.b * a.S * a.H + wi.h) * D));
     const uint64_t v_head = uniform_u64((uint64_t)((const bf16*)a.v + (wi.b * a.S * a.H + wi.h) * D));
-    const uint64_t slab_stride = (uint64_t)a.L * (uint64_t)row_bytes;
-    const int slab_bytes = __builtin_amdgcn_readfirstlane((L - 1) * row_bytes + D * 2);
+    auto slot_bytes = [&](int t) { return (uint64_t)mem_slot(strided, a.N, a.L, t, 0) * (uint64_t)row_bytes; };
+    const int64_t span_bytes = (int64_t)(L - 1) * rstride + D * 2;
 
     // Rounds: in round r device d holds the block of device (d - r) mod N.
     auto source = [&](int r) { return (d - r + a.N) % a.N; };
@@ -118,7 +121,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     const bool row_ok = j < L;
     const bool wave_live = jw0 < L;
     const int jw_last = min(jw0 + 31, L - 1);
-    const int64_t row = (slot0 + min(j, L - 1)) * a.H + wi.h;
+    const int64_t row = (wi.b * a.S + mem_slot(strided, a.N, a.L, d, min(j, L - 1))) * a.H + wi.h;
 
     // Q^T and dO^T operands (lane: query c32, dims kk*16 + 8*h2 .. +7).
     bf16x8 qreg[8], doreg[8];
@@ -131,7 +134,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
             doreg[kk] = dp[2 * kk];
         }
     }
-    const int64_t srow = (wi.b * a.H + wi.h) * a.S + (int64_t)d * a.L + min(j, L - 1);
+    const int64_t srow = (wi.b * a.H + wi.h) * a.S + mem_slot(strided, a.N, a.L, d, min(j, L - 1));
     const float2 st2 = *(const float2*)(a.stats + 2 * srow);
     const float lse_l2 = row_ok ? st2.x : 0.f;
     const float dlt = row_ok ? st2.y : 0.f;
@@ -148,20 +151,20 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     // chunk kc) -- four 16-byte loads per thread, written row-major.
     const int kq = tid & 15, dc = tid >> 4;
     const int kr = tid >> 2, kcc = tid & 3;
-    const int k_voff = 4 * kq * row_bytes + dc * 16;
-    const int v_voff = kr * row_bytes + kcc * 64;
+    const int k_voff = 4 * kq * rstride + dc * 16;
+    const int v_voff = kr * rstride + kcc * 64;
     const int kt_col = 16 * (kq >> 2) + 4 * ((kq & 1) * 2 + ((kq >> 1) & 1));
     u32x4 kst[4], vst[4];
 
     auto load_tile = [&](int s, int kt, bool valid) {
-        const int tile_off = kt * QBN * row_bytes;
-        int left = slab_bytes - tile_off;
-        left = (valid && left > 0) ? left : 0;
-        const uint64_t so = (uint64_t)s * slab_stride + (uint64_t)tile_off;
+        const int64_t tile_off = (int64_t)kt * QBN * rstride;
+        const int64_t left64 = span_bytes - tile_off;
+        const int left = (valid && left64 > 0) ? (int)min(left64, (int64_t)QBN * rstride) : 0;
+        const uint64_t so = slot_bytes(s) + (uint64_t)tile_off;
         const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const void*)(k_head + so), left);
         const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const void*)(v_head + so), left);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kst[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + i * row_bytes, 0, 0);
+        for (int i = 0; i < 4; ++i) kst[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + i * rstride, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) vst[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + 16 * i, 0, 0);
     };
@@ -301,8 +304,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     const uint64_t q_head = uniform_u64((uint64_t)((const bf16*)a.q + (wi.b * a.S * a.H + wi.h) * D));
     const uint64_t do_head = uniform_u64((uint64_t)((const bf16*)a.dout + (wi.b * a.S * a.H + wi.h) * D));
     const uint64_t st_head = uniform_u64((uint64_t)(a.stats + 2 * (wi.b * a.H + wi.h) * a.S));
-    const uint64_t slab_stride = (uint64_t)a.L * (uint64_t)row_bytes;
-    const int slab_bytes = __builtin_amdgcn_readfirstlane((L - 1) * row_bytes + D * 2);
+    // Device t's j-th token sits at slot mem_slot(t, j); consecutive tokens of
+    // a device are rstep slots (rstride bytes) apart.
+    const bool strided = a.strided != 0;
+    const int rstep = strided ? a.N : 1;
+    const int rstride = rstep * row_bytes;
+    const int64_t span_bytes = (int64_t)(L - 1) * rstride + D * 2;
     const int nqt = (L + KBQ - 1) / KBQ;
 
     // Rounds: in round r the block of device s meets the queries of device
@@ -322,7 +329,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     const int kw = kw0 + c32;
     const bool key_ok = kw < L;
     const bool wave_live = kw0 < L;
-    const int64_t krow = (wi.b * a.S + (int64_t)s * a.L + min(kw, L - 1)) * a.H + wi.h;
+    const int64_t krow = (wi.b * a.S + mem_slot(strided, a.N, a.L, s, min(kw, L - 1))) * a.H + wi.h;
 
     // K^T and V^T operands (lane: key c32, dims kk*16 + 8*h2 .. +7).
     bf16x8 kreg[8], vreg[8];
@@ -351,18 +358,20 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
     // lane l writes row 4i + l/16, slot l % 16, loading the chunk that slot
     // holds (for these rows swz = 4 (l/16) + w). Each wave also loads the
     // tile's 64 statistics floats into its own copy.
-    const int ld_voff = (4 * w + (lane >> 4)) * row_bytes + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | w));
-    const int ld_step = 16 * row_bytes;
+    const int ld_voff = (4 * w + (lane >> 4)) * rstride + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | w));
+    const int ld_step = 16 * rstride;
+    const int st_voff = (lane >> 1) * rstep * 8 + (lane & 1) * 4;   // lane: row lane/2, (LSE, Delta)[lane % 2]
     auto load_tile = [&](int r, int tq, bool valid, int stage) {
         const int dq = qdev(r);
-        const int tile_off = tq * KBQ * row_bytes;
-        int left = slab_bytes - tile_off;
-        left = (valid && left > 0) ? left : 0;
-        const uint64_t off = (uint64_t)dq * slab_stride + (uint64_t)tile_off;
+        const int64_t tile_off = (int64_t)tq * KBQ * rstride;
+        const int64_t left64 = span_bytes - tile_off;
+        const int left = (valid && left64 > 0) ? (int)min(left64, (int64_t)KBQ * rstride) : 0;
+        const uint64_t off = (uint64_t)mem_slot(strided, a.N, a.L, dq, 0) * (uint64_t)row_bytes + (uint64_t)tile_off;
         const i32x4 rq = raw_rsrc(q_head + off, left);
         const i32x4 rd = raw_rsrc(do_head + off, left);
-        const int srow0 = dq * L + tq * KBQ;                  // first row of the tile within the head
-        const int st_left = valid ? min(256, (a.N * L - srow0) * 8) : 0;
+        const int64_t srow0 = mem_slot(strided, a.N, a.L, dq, tq * KBQ);   // slot of the tile's first row
+        const int64_t st64 = (a.S - srow0) * 8;
+        const int st_left = valid ? (int)min(st64, (int64_t)KBQ * rstep * 8) : 0;
         const i32x4 rst = raw_rsrc(st_head + (uint64_t)srow0 * 8, st_left);
         const uint32_t dsq = lds_addr(&sm.q[stage][512 * w]);
         const uint32_t dsd = lds_addr(&sm.dout[stage][512 * w]);
@@ -370,7 +379,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv(BwdArgs a) {
         load_lds_b128(rq, ld_voff + ld_step, dsq + 4096);
         load_lds_b128(rd, ld_voff, dsd);
         load_lds_b128(rd, ld_voff + ld_step, dsd + 4096);
-        load_lds_b32(rst, 4 * lane, lds_addr(&sm.st[stage][w][0]));
+        load_lds_b32(rst, st_voff, lds_addr(&sm.st[stage][w][0]));
     };
 
     // Transposing-read addressing (lane (g, j) names key row 16 kk2 + 8 rd +

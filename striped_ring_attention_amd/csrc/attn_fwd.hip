@@ -173,12 +173,18 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
 
     const int rs = (int)(a.H * D);   // elements between consecutive slots
     const int row_bytes = rs * 2;
-    const bf16* __restrict__ qp0 = (const bf16*)a.q + ((blk.b * a.S + blk.d * a.L) * a.H + blk.h) * D;
-    // Slab of device s for this (b, h) starts at kv_head + s * slab_stride bytes.
+    // Device t's j-th token sits at slot mem_slot(t, j): consecutive tokens of
+    // a device are rstep slots (rstride bytes) apart.
+    const bool strided = a.strided != 0;
+    const int64_t rstep = strided ? a.N : 1;
+    const int rstride = (int)rstep * row_bytes;   // the host bounds a key tile's span below 2^31
+    const bf16* __restrict__ qp0 =
+        (const bf16*)a.q + ((blk.b * a.S + mem_slot(strided, a.N, a.L, blk.d, 0)) * a.H + blk.h) * D;
+    // Device s's tokens of this (b, h) start at kv_head + slot_bytes(s).
     const uint64_t kv_head_k = uniform_u64((uint64_t)((const bf16*)a.k + (blk.b * a.S * a.H + blk.h) * D));
     const uint64_t kv_head_v = uniform_u64((uint64_t)((const bf16*)a.v + (blk.b * a.S * a.H + blk.h) * D));
-    const uint64_t slab_stride = (uint64_t)a.L * (uint64_t)row_bytes;
-    const int slab_bytes = __builtin_amdgcn_readfirstlane((L - 1) * row_bytes + D * 2);
+    auto slot_bytes = [&](int s) { return (uint64_t)mem_slot(strided, a.N, a.L, s, 0) * (uint64_t)row_bytes; };
+    const int64_t span_bytes = (int64_t)(L - 1) * rstride + D * 2;   // first to last token of a device
 
     // This wave's 32 rows and live-key bounds (live keys of a row form a prefix).
     const int jw0 = j0 + w * 32;
@@ -191,7 +197,7 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     // the end read a valid row; they are fully masked and never written.
     bf16x8 qreg[8];
     {
-        const bf16x8* qp = (const bf16x8*)(qp0 + min(j, L - 1) * rs) + h2;
+        const bf16x8* qp = (const bf16x8*)(qp0 + (int64_t)min(j, L - 1) * rstep * rs) + h2;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) qreg[kk] = qp[2 * kk];
         // Let the Q loads land before any K/V load is issued: later waits on
@@ -220,16 +226,16 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     const int wg = w & 3;
     const int ld_row = 4 * wg + (lane >> 4);
     const int ld_sw = grp == 0 ? (ld_row & 15) : 4 * (lane >> 4);
-    const int ld_voff = ld_row * row_bytes + 16 * ((lane & 15) ^ ld_sw);
-    const int ld_step = 16 * row_bytes;
+    const int ld_voff = ld_row * rstride + 16 * ((lane & 15) ^ ld_sw);
+    const int ld_step = 16 * rstride;
     const uint64_t ld_head = uniform_u64(grp == 0 ? kv_head_k : kv_head_v);
     bf16* const ld_lds0 = (grp == 0 ? &sm.k[0][0] : &sm.v[0][0]) + 512 * wg;
 
     auto load_tile = [&](const TileCursor& c, bool valid, int stage) {
-        const int tile_off = c.kt * BN * row_bytes;
-        int left = slab_bytes - tile_off;
-        left = (valid && left > 0) ? left : 0;
-        const uint64_t base = ld_head + (uint64_t)c.s * slab_stride + (uint64_t)tile_off;
+        const int64_t tile_off = (int64_t)c.kt * BN * rstride;
+        const int64_t left64 = span_bytes - tile_off;
+        const int left = (valid && left64 > 0) ? (int)min(left64, (int64_t)BN * rstride) : 0;
+        const uint64_t base = ld_head + slot_bytes(c.s) + (uint64_t)tile_off;
         const i32x4 rsrc = raw_rsrc(base, left);
         const uint32_t dst = lds_addr(ld_lds0 + stage * (BN * D));
 #pragma unroll
@@ -399,7 +405,7 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     const float lse_b = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     if (!row_ok) return;
 
-    const int64_t row = (blk.b * a.S + blk.d * a.L + j) * a.H + blk.h;   // (b, slot, h) row index
+    const int64_t row = (blk.b * a.S + mem_slot(strided, a.N, a.L, blk.d, j)) * a.H + blk.h;   // (b, slot, h) row
     float wa = 0.f, wb = 1.f, l_out = lse_b;
     if (!kFused && (flags & kFlagMerge)) {
         const float la = a.lse_acc[row];
@@ -453,12 +459,13 @@ __global__ void __launch_bounds__(64) round_fwd_f32(RoundArgs a, int flags) {
     const float* __restrict__ q = (const float*)a.q;
     const float* __restrict__ kg = (const float*)a.k;
     const float* __restrict__ vg = (const float*)a.v;
-    const int64_t row_stride = H * DH;
-    const int64_t kv_base = ((blk.b * S + blk.s * L) * H + blk.h) * DH;
+    const bool strided = a.strided != 0;
+    const int64_t row_stride = (strided ? a.N : 1) * H * DH;   // between consecutive keys of a device
+    const int64_t kv_base = ((blk.b * S + mem_slot(strided, a.N, L, blk.s, 0)) * H + blk.h) * DH;
     const int64_t j = j0 + lane;
     const bool row_ok = j < L;
     const int64_t c_row = row_ok ? live_keys(j, blk.delta, L) : 0;
-    const int64_t row = (blk.b * S + blk.d * L + (row_ok ? j : 0)) * H + blk.h;
+    const int64_t row = (blk.b * S + mem_slot(strided, a.N, L, blk.d, row_ok ? j : 0)) * H + blk.h;
 
     float qr[DH], o[DH];
 #pragma unroll

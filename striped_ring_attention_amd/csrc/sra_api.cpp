@@ -53,6 +53,8 @@ int check_desc(const sra_desc* d) {
         return fail(SRA_ERR_INVALID_ARG, "dtype %d is neither f32 (0) nor bf16 (1)", d->dtype);
     if (d->schedule != SRA_SCHEDULE_PER_ROUND && d->schedule != SRA_SCHEDULE_FUSED)
         return fail(SRA_ERR_INVALID_ARG, "schedule %d unknown", d->schedule);
+    if (d->order != SRA_ORDER_DEVICE && d->order != SRA_ORDER_ORIGINAL)
+        return fail(SRA_ERR_INVALID_ARG, "order %d is neither device (0) nor original (1)", d->order);
     if (!(d->scale >= 0.f) || std::isinf(d->scale))
         return fail(SRA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 = 1/sqrt(head_dim))");
     // Element counts must fit comfortably in int64 and the grid in 32 bits.
@@ -69,6 +71,13 @@ int check_desc(const sra_desc* d) {
     const double slab = (double)(L + 2 * sra::kBf16TileK) * (double)d->heads * (double)d->head_dim * 4.0;
     if (slab > 2147483647.0) return fail(SRA_ERR_UNSUPPORTED, "a device slab of %lld tokens x %lld heads is too large for 32-bit offsets",
                                          (long long)L, (long long)d->heads);
+    // In original order a device's consecutive tokens are N rows apart: one
+    // key tile (plus a tile of look-ahead) must still span < 2^31 bytes.
+    const double tile_span = (double)(2 * sra::kBf16TileK + 1) * (double)d->n_dev * (double)d->heads *
+                             (double)d->head_dim * 4.0;
+    if (d->order == SRA_ORDER_ORIGINAL && tile_span > 2147483647.0)
+        return fail(SRA_ERR_UNSUPPORTED, "in original order %d devices x %lld heads is too wide for 32-bit tile offsets",
+                    d->n_dev, (long long)d->heads);
     const int64_t tq = d->dtype == SRA_DTYPE_BF16 ? sra::kBf16TileQ : sra::kF32TileQ;
     const double blocks = (double)((L + tq - 1) / tq) * (double)d->heads * (double)d->n_dev * (double)d->batch;
     if (blocks > 2147483647.0) return fail(SRA_ERR_INVALID_ARG, "problem needs more than 2^31 workgroups per round");
@@ -88,6 +97,7 @@ sra::RoundArgs make_args(const sra_desc* d, const void* q, const void* k, const 
     a.L = d->seq / d->n_dev;
     a.N = d->n_dev;
     a.layout = d->layout;
+    a.strided = d->order == SRA_ORDER_ORIGINAL && d->layout == SRA_LAYOUT_STRIPED;
     a.scale = eff_scale(d);
     a.scale_log2 = (float)((double)a.scale * 1.4426950408889634074);
     return a;
@@ -372,6 +382,7 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
     a.L = desc->seq / desc->n_dev;
     a.N = desc->n_dev;
     a.layout = desc->layout;
+    a.strided = desc->order == SRA_ORDER_ORIGINAL && desc->layout == SRA_LAYOUT_STRIPED;
     a.scale = eff_scale(desc);
     a.scale_log2 = (float)((double)a.scale * 1.4426950408889634074);
     return hip_status(sra::launch_bwd_bf16_d128(a, (hipStream_t)stream), "ring backward launch");

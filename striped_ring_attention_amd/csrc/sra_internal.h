@@ -32,8 +32,17 @@ __host__ __device__ inline int64_t live_keys(int64_t j, int64_t delta, int64_t L
     return c < 0 ? 0 : (c > L ? L : c);
 }
 
-// Launchers (each returns hipSuccess or the launch error). All tensors are in
-// device layout [B, S, H, Dh]; see sra.h for argument meaning.
+// Memory slot (row along the sequence axis) of device d's j-th token: d*L + j
+// in device layout, and also in original order with the contiguous layout;
+// j*N + d in original order with the striped layout ("strided": a device's
+// tokens are every N-th row).
+__host__ __device__ inline int64_t mem_slot(bool strided, int64_t N, int64_t L, int64_t d, int64_t j) {
+    return strided ? j * N + d : d * L + j;
+}
+
+// Launchers (each returns hipSuccess or the launch error). Tensors are
+// [B, S, H, Dh] with device d's j-th token at slot mem_slot(...); see sra.h
+// for argument meaning.
 struct RoundArgs {
     const void* q;
     const void* k;
@@ -46,6 +55,7 @@ struct RoundArgs {
     int32_t N, layout, round, dev_lo, dev_hi;   // query devices [dev_lo, dev_hi)
     float scale;         // softmax scale
     float scale_log2;    // softmax scale * log2(e)
+    int32_t strided;     // 1: tensors in original order with the striped layout (see mem_slot)
     int32_t mode;        // 0: write the partial to (o_acc, lse_acc); 1: merge it into them;
                          // 2: merge and write the output to o_final (dtype) and lse_acc;
                          // 3: write the partial as the output (o_final, lse_acc)
@@ -61,12 +71,13 @@ struct BwdArgs {
     const void* o;
     const float* lse;     // fp32 [B,S,H], natural log
     const void* dout;
-    float* stats;         // fp32 [B,H,S,2] workspace: per row (LSE * log2 e, rowsum(dO * O))
+    float* stats;         // fp32 [B,H,S,2] workspace: per memory slot (LSE * log2 e, rowsum(dO * O))
     void* dq;
     void* dk;
     void* dv;
     int64_t B, S, H, L;
     int32_t N, layout;
+    int32_t strided;      // 1: tensors in original order with the striped layout (see mem_slot)
     float scale;
     float scale_log2;
 };

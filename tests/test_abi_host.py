@@ -125,10 +125,10 @@ FAKE2 = ctypes.c_void_p(1 << 30)
 
 def desc(**kw):
     base = dict(batch=1, seq=64, heads=2, head_dim=128, n_dev=4, layout=1, dtype=sra.DTYPE_BF16, scale=0.0,
-                schedule=0)
+                schedule=0, order=0)
     base.update(kw)
     return sra.make_desc(base["batch"], base["seq"], base["heads"], base["head_dim"], base["n_dev"],
-                         base["layout"], base["dtype"], base["scale"], base["schedule"])
+                         base["layout"], base["dtype"], base["scale"], base["schedule"], base["order"])
 
 
 def rr(lib, d, rnd=0, dev=-1, q=FAKE, k=FAKE, v=FAKE, o=FAKE2, l=FAKE2):
@@ -147,6 +147,11 @@ def test_invalid_descriptors_rejected(lib):
     assert rr(lib, desc(scale=-1.0)) == INVALID
     assert rr(lib, desc(scale=float("inf"))) == INVALID
     assert rr(lib, desc(schedule=5)) == INVALID
+    assert rr(lib, desc(order=2)) == INVALID
+    assert rr(lib, desc(order=-1)) == INVALID
+    assert b"order" in lib.sra_last_error()
+    # original order: one key tile must span < 2^31 bytes (devices x heads x head_dim)
+    assert rr(lib, desc(order=1, seq=4096 * 512, n_dev=4096, heads=512)) == UNSUPPORTED
     assert rr(lib, desc(head_dim=64)) == UNSUPPORTED     # bf16 kernel is Dh=128 only
     assert rr(lib, desc(head_dim=96, dtype=sra.DTYPE_F32)) == UNSUPPORTED
     assert b"head_dim" in lib.sra_last_error()
