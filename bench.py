@@ -40,14 +40,16 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
 FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
-# HBM traffic of one fused forward launch on the Short workload (striped),
+# HBM traffic of one fused forward launch on the Short workload (striped,
+# tensors in the order named),
 # from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by the same counters
 # on the stripe-permute copy kernel of known size; filled in from the counter
 # summary under profiles/ and valid only for the kernel sources it was taken on.
-TRAFFIC = {"workload": "short", "kernel_sources_sha256": "44efbe1d32557bfe430094a26be3efc56df27184e80507a9ba570ce1723a51e5",
-           "bytes_per_launch": 1032637329,
-           "fetch_bytes_per_launch": 996751043, "write_bytes_per_launch": 35886286,
-           "copy_scale": {"FETCH_SIZE": 1.99700, "WRITE_SIZE": 0.99953}}
+TRAFFIC = {"workload": "short", "order": "original",
+           "kernel_sources_sha256": "a428794dc398d9c6749e18208e285b4a08e6f562029bfa431d743a789411d1a1",
+           "bytes_per_launch": 926078824,
+           "fetch_bytes_per_launch": 890409232, "write_bytes_per_launch": 35669592,
+           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99977}}
 
 
 def parse():
@@ -116,19 +118,19 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload, sched, layout):
+def stored_traffic(workload, sched, layout, order):
     """HBM bytes per launch of the fused forward kernel from the last counter
     runs, or None when they do not cover this configuration or the kernel's
     sources have changed since they were taken."""
     t = TRAFFIC
-    if (t is None or workload != t["workload"] or sched != 1 or layout != 1
+    if (t is None or workload != t["workload"] or sched != 1 or layout != 1 or order != t["order"]
             or kernel_source_digest() != t["kernel_sources_sha256"]):
         return None
     return t["bytes_per_launch"]
 
 
-def traffic_detail(workload, sched, layout):
-    if stored_traffic(workload, sched, layout) is None:
+def traffic_detail(workload, sched, layout, order):
+    if stored_traffic(workload, sched, layout, order) is None:
         return None
     return {k: TRAFFIC[k] for k in ("fetch_bytes_per_launch", "write_bytes_per_launch", "copy_scale")}
 
@@ -356,10 +358,10 @@ def main():
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": stored_traffic(args.workload, sched, layout),
+                     "traffic": stored_traffic(args.workload, sched, layout, args.order),
                      "kernel": "round_fwd_bf16_d128<fused>" if sched == sra.SCHEDULE_FUSED
                      else "round_fwd_bf16_d128<per-round>",
-                     "traffic_detail": traffic_detail(args.workload, sched, layout),
+                     "traffic_detail": traffic_detail(args.workload, sched, layout, args.order),
                      "launches_per_step": nl, "avg_launch_ms": attn_ms / nl,
                      "flops_per_launch": flops_per_launch},
         "imbalance": imb, "permutation": perm, "compare": compare, "backward": backward,
