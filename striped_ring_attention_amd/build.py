@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsra.so")
 
-SOURCES = ["sra_api.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["sra_api.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -31,15 +31,20 @@ COMMON = [
 ]
 
 
-# Per-source flags. The attention kernels run with the IEEE mode bit off
-# (no NaN quieting around min/max; infinities still behave) so the row max
-# compiles to bare v_max3_f32.
-# The attention kernels run with IEEE mode off (v_max3 without NaN quieting)
-# and with the latency-oriented ILP scheduler, which keeps LDS operand reads a
-# step ahead of the MFMAs that consume them (the default occupancy-oriented
-# scheduler reuses one operand register set and waits on every read).
-PER_SOURCE = {n: ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-              for n in ("attn_fwd.hip", "attn_bwd.hip")}
+# Per-source flags. The attention kernels run with the IEEE mode bit off (no
+# NaN quieting around min/max; infinities still behave), so the row max
+# compiles to bare v_max3_f32. The forward and dQ kernels use the
+# latency-oriented ILP scheduler, which keeps LDS operand reads a step ahead of
+# the MFMAs that consume them (the default occupancy-oriented scheduler reuses
+# one operand register set and waits on every read). The dK/dV kernel orders
+# its reads explicitly and is register-bound at two waves per SIMD; it uses the
+# register-minimising scheduler, the one that leaves it without spills.
+_IEEE_OFF = ["-mno-amdgpu-ieee", "-fno-honor-nans"]
+PER_SOURCE = {
+    "attn_fwd.hip": _IEEE_OFF + ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "attn_bwd.hip": _IEEE_OFF + ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "attn_bwd_dkdv.hip": _IEEE_OFF + ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
+}
 
 
 def _compile(src, extra):

@@ -66,14 +66,35 @@ def project(t_striped, t_contig, block_bytes, link_gbps=DEFAULT_LINK_GBPS):
 def time_device_rounds(q, k, v, n_dev, layout, reps=3):
     """t[r][d] in ms: one launch per (round, device) on device-layout q, k, v,
     bracketed by events on the current stream; median over `reps` after one
-    warm-up pass."""
+    warm-up pass.
+
+    A short launch can take less GPU time than the host needs to enqueue it;
+    an event pair around it would then also measure the host. Each timed pass
+    therefore starts behind a queue of matrix products sized from the warm-up
+    pass to outlast the host's enqueueing, so the launches run back to back."""
+    import math
+    import time
     import torch
     import striped_ring_attention_amd as sra
     B, S, H, D = q.shape
     o = torch.empty((B, S, H, D), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, S, H), dtype=torch.float32, device=q.device)
+    pad = torch.ones((4096, 4096), dtype=torch.bfloat16, device=q.device)
     samples = [[[] for _ in range(n_dev)] for _ in range(n_dev)]
+    n_pad, host_s = 0, 0.0
     for rep in range(reps + 1):
+        if rep == 1:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(8):
+                torch.mm(pad, pad)
+            b.record()
+            torch.cuda.synchronize()
+            pad_ms = a.elapsed_time(b) / 8
+            n_pad = math.ceil(2.0 * host_s * 1e3 / max(pad_ms, 1e-3)) + 1
+        for _ in range(n_pad):
+            torch.mm(pad, pad)
+        t0 = time.perf_counter()
         evs = []
         for r in range(n_dev):
             for d in range(n_dev):
@@ -82,6 +103,7 @@ def time_device_rounds(q, k, v, n_dev, layout, reps=3):
                 sra.ring_round_attn(q, k, v, n_dev, layout, r, device=d, o_part=o, lse_part=lse)
                 b.record()
                 evs.append((r, d, a, b))
+        host_s = time.perf_counter() - t0
         torch.cuda.synchronize()
         if rep == 0:
             continue
