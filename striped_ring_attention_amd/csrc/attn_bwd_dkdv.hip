@@ -29,7 +29,7 @@ struct __align__(16) SmemDkdv {
     bf16 q[DK_NS][KBQ * D];       // Q tiles
     bf16 dout[DK_NS][KBQ * D];    // dO tiles
     float st[DK_NS][8][64];       // per wave: LSE log2 e of the tile's 32 rows, then their Delta
-    f32x4 p[4][4][64];            // P of the latest tile, per key group: [group][register quad][lane]
+    f32x4 p[2][4][4][64];         // P of tiles t (slot t % 2) and t-1: [slot][group][register quad][lane]
 };
 
 // A workgroup owns 128 keys of one source device and walks, round by round,
@@ -38,16 +38,18 @@ struct __align__(16) SmemDkdv {
 // one SIMD (waves g and g + 4):
 //   the P wave holds K^T and dV: S = Q K^T, P = 2^(S scale log2 e - LSE log2 e),
 //     dV^T += dO^T P;
-//   the dS wave holds V^T and dK: dP = dO V^T, dS = P (dP - Delta) scale,
-//     dK^T += Q^T dS,
-// with P (fp32) handed over through LDS. Each tile step has two phases
-// separated by barriers, and the two waves of a SIMD alternate between
-// matrix and vector work:
-//   phase A(t): P wave: dV += (tile t-1), S of tile t       (16 MFMAs)
-//               dS wave: dS of tile t-1 from P and dP       (vector)
-//   phase B(t): P wave: P of tile t, written to LDS         (vector)
-//               dS wave: dK += (tile t-1), dP of tile t     (16 MFMAs)
-// Each wave holds half the accumulators a single wave would need. Q and dO
+//   the dS wave holds V^T and dK: dP = dO V^T, dS = P (dP - Delta),
+//     dK^T += Q^T dS, times the softmax scale once at the end,
+// with P (fp32) handed over through LDS. In tile step t the two waves of a
+// SIMD do their matrix and vector work in opposite order, so that one's
+// vector work runs under the other's MFMAs:
+//   P wave:  dV += (tile t-1), S of tile t (16 MFMAs); then P of tile t (vector)
+//   dS wave: dS of tile t-1 from P and dP (vector); then dK += (tile t-1),
+//            dP of tile t (16 MFMAs)
+// P is double-buffered in LDS (tile t in slot t % 2), so the dS wave reads
+// P of tile t-1 while the P wave writes P of tile t, and one barrier per step
+// (for the tile ring and P) suffices. Each wave holds half the accumulators
+// a single wave would need. Q and dO
 // rows are read from LDS as MFMA row operands and, for dV and dK, transposed
 // through ds_read_b64_tr_b16. Tiles stream into a 7-stage LDS ring five
 // tiles ahead; tiles t-1 and t are read during step t.
@@ -108,14 +110,13 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     const int64_t krow = (wi.b * a.S + mem_slot(strided, N, a.L, s, min(kw, L - 1))) * a.H + wi.h;
 
     // K^T (P wave) or V^T (dS wave) operand: lane holds key c32, dims
-    // kk*16 + 8*h2 .. +7. Loaded before any tile load is issued, so that
-    // waiting for it never waits for the tile stream.
+    // kk*16 + 8*h2 .. +7. Issued before the first tile loads and awaited
+    // together with them (one memory round trip before the loop).
     bf16x8 kvreg[8];
     {
         const bf16x8* kp = (const bf16x8*)((const bf16*)(ds_wave ? a.v : a.k) + krow * D) + h2;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) kvreg[kk] = kp[2 * kk];
-        __builtin_amdgcn_s_waitcnt(0);
     }
 
     // Loads: wave w issues instruction w of each 8-instruction (8 KiB) tile of
@@ -172,8 +173,9 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     // Row-operand addressing: lane (c32, h2) reads chunk 2 kk + h2 of row c32.
     auto row_off = [&](int kk) { return c32 * D + 8 * ((2 * kk + h2) ^ swz(c32)); };
 
-    // Zero LDS once (rows past a slab end are never loaded), then tiles 0..3.
-    {
+    // When a slab ends inside a query tile, zero LDS once (rows past a slab
+    // end are never loaded and must hold finite values). Then tiles 0..4.
+    if (L % KBQ != 0) {
         u32x4* z = (u32x4*)&sm;
         for (int i = tid; i < (int)(sizeof(SmemDkdv) / 16); i += DK_NT) z[i] = u32x4{0u, 0u, 0u, 0u};
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -181,12 +183,12 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     }
 #pragma unroll 1
     for (int u = 0; u < DK_AHEAD; ++u) load_tile(u < n_tiles, u);
-    __builtin_amdgcn_s_waitcnt(kWaitVm12);   // tile 0 is in
+    __builtin_amdgcn_s_waitcnt(0);   // the K/V operands and tiles 0..4 are in
     bar();
 
     const float sl = a.scale_log2;
     const float scale = a.scale;
-    f32x4* const pex = sm.p[kg][0] + lane;   // this lane's P quads: pex[64 g]
+    auto pex = [&](int t) { return sm.p[t & 1][kg][0] + lane; };   // this lane's P quads of tile t: [64 g]
     auto next_stage = [](int x) { return x + 1 == DK_NS ? 0 : x + 1; };
 
     // Operand reads. Transposed: 8 operands (two 16-row halves x 4 dim
@@ -234,8 +236,9 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     // while its dP MFMAs run. Reads are issued whether or not the tile has
     // work for the group (every address is valid), which keeps the compiler's
     // LDS wait counting exact. Only the P wave's writes need an LDS wait before
-    // a barrier; every other read is consumed before its stage is refilled
-    // two steps later.
+    // the step's barrier; every other read is consumed before its stage is
+    // refilled two steps later. (Phase A and B below name the two halves of
+    // each wave's step.)
     int cr = 0, cq = first_tile(0);
     settle(cr, cq);
     int c_delta = delta_of(cr);
@@ -279,7 +282,6 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             if (act_prev) acc_t(yt, opb);
             if (act) x = rows_kv(xr);
-            bar();
             // Phase B: P of tile t, written for the dS wave; dO^T of tile t read.
             read_yt(sm.dout[stg], yt);
             __builtin_amdgcn_sched_barrier(0);
@@ -303,7 +305,7 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
                         pq[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], sl, -lz[g][e]));
                         opb[i >> 3][i & 7] = (bf16)pq[e];
                     }
-                    pex[64 * g] = pq;
+                    pex(t)[64 * g] = pq;
                 }
             }
             step_end(t, act);
@@ -320,7 +322,7 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
                 const float* stp = sm.st[stg_prev][w];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    pq[g] = pex[64 * g];
+                    pq[g] = pex(t - 1)[64 * g];
                     dz[g] = *(const f32x4*)&stp[32 + 8 * g + 4 * h2];
                 }
             }
@@ -329,9 +331,8 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
             if (act_prev) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    opb[i >> 3][i & 7] = (bf16)(pq[i >> 2][i & 3] * (x[i] - dz[i >> 2][i & 3]) * scale);
+                    opb[i >> 3][i & 7] = (bf16)(pq[i >> 2][i & 3] * (x[i] - dz[i >> 2][i & 3]));
             }
-            bar();
             // Phase B: dP of tile t, dK^T += Q^T dS (tile t-1); the Q^T reads
             // land while the dP MFMAs run.
             bf16x8 yt[2][4];
@@ -346,14 +347,16 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);   // no load may still be writing LDS when the workgroup ends
 
     if (!key_ok) return;
+    // dK carries the softmax scale once here (its dS operands leave it out).
+    const float osc = ds_wave ? scale : 1.0f;
     bf16* outp = (bf16*)(ds_wave ? a.dk : a.dv) + krow * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int dcol = db * 32 + 8 * g + 4 * h2;
-            const bf16x4 v4 = {(bf16)acc[db][4 * g], (bf16)acc[db][4 * g + 1], (bf16)acc[db][4 * g + 2],
-                               (bf16)acc[db][4 * g + 3]};
+            const bf16x4 v4 = {(bf16)(acc[db][4 * g] * osc), (bf16)(acc[db][4 * g + 1] * osc),
+                               (bf16)(acc[db][4 * g + 2] * osc), (bf16)(acc[db][4 * g + 3] * osc)};
             *(bf16x4*)(outp + dcol) = v4;
         }
 }
