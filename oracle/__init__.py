@@ -24,10 +24,13 @@ Modules:
   stripes    -- stripe/contiguous position maps and brute-force tile census.
   attention  -- dense causal attention, per-round ring partials, the
                 log-sum-exp merge, the full ring and the backward pass.
+  rotary     -- rotary position embedding of model inputs at their original
+                positions, and its composition with the stripe gather.
 
 Parity status of each function is stated in its docstring; every function
-here is pinned by ``tests/test_oracle.py`` (brute force, closed forms,
-invariants, a library special case) -- none is "parity unpinned".
+here is pinned by ``tests/test_oracle.py`` and ``tests/test_oracle_rope.py``
+(brute force, closed forms, invariants, a library special case) -- none is
+"parity unpinned".
 """
 
 from .stripes import (  # noqa: F401
@@ -52,4 +55,9 @@ from .attention import (  # noqa: F401
     dense_causal_backward,
     backward_key_rows,
     backward_query_rows,
+)
+from .rotary import (  # noqa: F401
+    inv_freq,
+    rope,
+    rope_device_layout,
 )
