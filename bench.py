@@ -28,6 +28,7 @@ cpu_baseline = the CPU oracle (fp64 numpy dense causal attention) on a
 import argparse
 import hashlib
 import json
+import statistics
 import os
 import sys
 import time
@@ -262,6 +263,7 @@ def main():
     ms_step, per_launch, perm_ev = timed(layout, sched, K, perm=dev_striped)
     wall = time.perf_counter() - wall0
     attn_ms = sum(sum(p) for p in per_launch) / K
+    ring_ms_steps = [sum(p) for p in per_launch]   # kernel time of each timed step
     nl = launches(sched)
     useful_flops = 4.0 * D * B * H * S * (S + 1) / 2
     value = useful_flops / (ms_step * 1e-3) / 1e12
@@ -291,6 +293,52 @@ def main():
         perm = {"stripe_permute_qkv_ms": p_ms, "stripe_permute_GBps": p_bytes / (p_ms * 1e-3) / 1e9,
                 "unstripe_o_lse_ms": u_ms, "unstripe_GBps": u_bytes / (u_ms * 1e-3) / 1e9,
                 "hbm_peak_GBps": PEAK_HBM_GBS, "note": "timed back to back inside the step (caches warm)"}
+
+    # Cold-cache rates: the 256 MB Infinity Cache is flushed (a 1 GiB write)
+    # before each repetition; median of 5.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.device)
+
+    def cold_ms(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    if layout == sra.STRIPED:
+        pq_out = torch.empty_like(q)
+        c_ms = cold_ms(lambda: sra.stripe_permute(q, N, out=pq_out))
+        perm["stripe_permute_cold_GBps"] = 2 * q.numel() * q.element_size() / (c_ms * 1e-3) / 1e9
+        perm["cold_note"] = "one tensor, Infinity Cache flushed before each of 5 runs, median"
+
+    # Model-input step (not part of value): rotary embedding of Q and K at their
+    # original positions, fused with the stripe gather (device layout).
+    qr_out, kr_out = torch.empty_like(q), torch.empty_like(k)
+
+    def rope_qk():
+        sra.rope_permute(q, N, layout, out=qr_out)
+        sra.rope_permute(k, N, layout, out=kr_out)
+
+    rope_qk()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(10):
+        rope_qk()
+    r1.record()
+    torch.cuda.synchronize()
+    r_ms = r0.elapsed_time(r1) / 10
+    r_bytes = 2 * 2 * q.numel() * q.element_size()
+    rc_ms = cold_ms(rope_qk)
+    model_input = {"rope_permute_qk_ms": r_ms, "rope_permute_GBps": r_bytes / (r_ms * 1e-3) / 1e9,
+                   "rope_permute_cold_GBps": r_bytes / (rc_ms * 1e-3) / 1e9, "hbm_peak_GBps": PEAK_HBM_GBS,
+                   "note": "Q and K rotated at original positions and gathered into the layout; not part of value"}
+    del flush
 
     # Imbalance: host census at 128x128 tiles and at the kernel's own tiles; device counters.
     tq, tk = sra.kernel_tiles(torch.bfloat16, D)
@@ -363,8 +411,10 @@ def main():
                      else "round_fwd_bf16_d128<per-round>",
                      "traffic_detail": traffic_detail(args.workload, sched, layout, args.order),
                      "launches_per_step": nl, "avg_launch_ms": attn_ms / nl,
+                     "step_kernel_ms_median_min_max": [statistics.median(ring_ms_steps), min(ring_ms_steps),
+                                                       max(ring_ms_steps)],
                      "flops_per_launch": flops_per_launch},
-        "imbalance": imb, "permutation": perm, "compare": compare, "backward": backward,
+        "imbalance": imb, "permutation": perm, "model_input": model_input, "compare": compare, "backward": backward,
         "critical_path": critical,
         "wall_s_timed": wall,
     }

@@ -144,6 +144,28 @@ int sra_stripe_permute(const void* x, void* y, int64_t outer, int64_t seq,
 int sra_unstripe(const void* y, void* x, int64_t outer, int64_t seq,
                  int64_t row_bytes, int32_t n_dev, void* stream);
 
+/* Rotary position embedding of a model input (Q or K), fused with the stripe
+ * gather. The pages stripe the inputs once, before the first layer
+ * ("Summary" ¶2; "Key points: Striped layout"); they say nothing about
+ * positional encodings, and a rotary encoding must see every token's
+ * original position whatever slot the token lands in. Each head vector of the
+ * token at original position t is rotated in "rotate half" form: pair
+ * (c, c + D/2), c < D/2, turns by a_c = p * base^(-2c/D), with p = pos[b*S + t]
+ * (device int64 [B, S] in original order) or p = t when pos is NULL:
+ *   y_c = x_c cos a_c - x_{c+D/2} sin a_c,  y_{c+D/2} = x_c sin a_c + x_{c+D/2} cos a_c.
+ * Angles are reduced modulo 2*pi in fp64 and evaluated in fp32; the rotation
+ * is computed in fp32 and stored in the dtype (bf16 rounded to nearest even).
+ * x: [B, S, H, D] in original order; y: same shape, in striped device layout
+ * (slot d*L + j holds the token at j*N + d) when desc->order is
+ * SRA_ORDER_DEVICE and the layout striped, else in original order (plain
+ * rotary embedding; in that case y may equal x, any other overlap is an
+ * error). Reads batch, seq, heads, head_dim, n_dev, layout, dtype and order of
+ * desc; head_dim a multiple of 8 up to 256; base finite and > 1 (10000 is
+ * the usual value). Token ids and any other per-token row are striped with
+ * sra_stripe_permute. */
+int sra_rope_permute(const sra_desc* desc, const void* x, void* y, const int64_t* pos, double base,
+                     void* stream);
+
 /* One ring round (round r in [0, N)) for query device `device` (or all
  * devices if device == -1): device d's queries attend to the K/V block of
  * device (d - r) mod N under the causal mask above, skipping tiles with no

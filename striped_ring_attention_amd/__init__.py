@@ -58,6 +58,7 @@ _PROTOS = {
     "sra_kernel_tiles": (_i32, [ctypes.POINTER(SraDesc), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "sra_stripe_permute": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "sra_unstripe": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _vp]),
+    "sra_rope_permute": (_i32, [ctypes.POINTER(SraDesc), _vp, _vp, _vp, ctypes.c_double, _vp]),
     "sra_ring_round_attn": (_i32, [ctypes.POINTER(SraDesc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "sra_lse_merge": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "sra_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SraDesc)]),
@@ -202,6 +203,19 @@ def unstripe(y, n_dev, out=None):
     _check_tensors(y, out)
     out = torch.empty_like(y) if out is None else out
     _check(lib().sra_unstripe(_ptr(y), _ptr(out), y.shape[0], y.shape[1], _row_bytes(y), n_dev, _stream()))
+    return out
+
+
+def rope_permute(x, n_dev, layout, pos=None, base=10000.0, order=ORDER_DEVICE, out=None):
+    """Rotary embedding of x ([B, S, H, D], original order) at each token's
+    original position (or pos, int64 [B, S]), written in striped device layout
+    (order=ORDER_DEVICE, striped) or in original order (out may be x then)."""
+    _check_tensors(x, out, pos)
+    if pos is not None and (pos.dtype != torch.int64 or tuple(pos.shape) != tuple(x.shape[:2])):
+        raise ValueError("pos must be int64 [B, S]")
+    d = _desc_for(x, n_dev, layout, 0.0, order=order)
+    out = torch.empty_like(x) if out is None else out
+    _check(lib().sra_rope_permute(ctypes.byref(d), _ptr(x), _ptr(out), _ptr(pos), float(base), _stream()))
     return out
 
 

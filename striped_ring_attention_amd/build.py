@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsra.so")
 
-SOURCES = ["sra_api.cpp", "permute.hip", "lse_merge.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip"]
+SOURCES = ["sra_api.cpp", "permute.hip", "lse_merge.hip", "rope.hip", "attn_fwd.hip", "attn_bwd.hip",
+           "attn_bwd_dkdv.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <initializer_list>
 
+#include "rope_internal.h"
 #include "sra_internal.h"
 
 namespace {
@@ -386,6 +387,47 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
     a.scale = eff_scale(desc);
     a.scale_log2 = (float)((double)a.scale * 1.4426950408889634074);
     return hip_status(sra::launch_bwd_bf16_d128(a, (hipStream_t)stream), "ring backward launch");
+}
+
+int sra_rope_permute(const sra_desc* desc, const void* x, void* y, const int64_t* pos, double base, void* stream) {
+    if (desc == nullptr) return fail(SRA_ERR_INVALID_ARG, "desc is NULL");
+    int st = check_layout(desc->seq, desc->n_dev, desc->layout);
+    if (st) return st;
+    if (desc->batch < 1 || desc->heads < 1) return fail(SRA_ERR_INVALID_ARG, "batch and heads must be >= 1");
+    if (desc->dtype != SRA_DTYPE_F32 && desc->dtype != SRA_DTYPE_BF16)
+        return fail(SRA_ERR_INVALID_ARG, "dtype %d is neither f32 (0) nor bf16 (1)", desc->dtype);
+    if (desc->order != SRA_ORDER_DEVICE && desc->order != SRA_ORDER_ORIGINAL)
+        return fail(SRA_ERR_INVALID_ARG, "order %d is neither device (0) nor original (1)", desc->order);
+    if (desc->head_dim < 8 || desc->head_dim > 2 * sra::kRopeMaxHalf || desc->head_dim % 8 != 0)
+        return fail(SRA_ERR_UNSUPPORTED, "rotary embedding needs head_dim a multiple of 8 in [8, %d], got %lld",
+                    2 * sra::kRopeMaxHalf, (long long)desc->head_dim);
+    if (!(base > 1.0) || std::isinf(base)) return fail(SRA_ERR_INVALID_ARG, "base must be finite and > 1");
+    if (!x || !y) return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(x) || !aligned16(y)) return fail(SRA_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if ((uintptr_t)pos & 7u) return fail(SRA_ERR_INVALID_ARG, "pos misaligned");
+    const double rows = (double)desc->batch * (double)desc->seq;
+    if (rows > 2147483647.0) return fail(SRA_ERR_INVALID_ARG, "batch * seq must be < 2^31");
+    const bool strided = desc->order == SRA_ORDER_DEVICE && desc->layout == SRA_LAYOUT_STRIPED;
+    const double total = rows * (double)desc->heads * (double)desc->head_dim * (desc->dtype == SRA_DTYPE_BF16 ? 2 : 4);
+    if (total > 4.0e18) return fail(SRA_ERR_INVALID_ARG, "tensor too large");
+    const uintptr_t a0 = (uintptr_t)x, a1 = a0 + (uintptr_t)total, b0 = (uintptr_t)y, b1 = b0 + (uintptr_t)total;
+    // In place is allowed when no row moves (every element is read and
+    // written by the same thread); any other overlap is rejected.
+    if (a0 < b1 && b0 < a1 && !(a0 == b0 && !strided))
+        return fail(SRA_ERR_INVALID_ARG, "x and y overlap (in place is allowed only when nothing is permuted)");
+    sra::RopeArgs a{};
+    a.x = x;
+    a.y = y;
+    a.pos = pos;
+    a.B = desc->batch;
+    a.S = desc->seq;
+    a.H = desc->heads;
+    a.L = desc->seq / desc->n_dev;
+    a.D = (int32_t)desc->head_dim;
+    a.N = desc->n_dev;
+    a.strided = strided;
+    for (int c = 0; c < a.D / 2; ++c) a.inv_freq[c] = std::pow(base, -2.0 * c / (double)a.D);
+    return hip_status(sra::launch_rope(a, desc->dtype == SRA_DTYPE_BF16, (hipStream_t)stream), "rope_permute launch");
 }
 
 }  // extern "C"

@@ -208,3 +208,29 @@ def test_invalid_host_calls_rejected(lib):
     assert lib.sra_count_live_tiles(ctypes.byref(d), 0, 16, buf, None, None) == INVALID
     assert lib.sra_count_live_tiles(ctypes.byref(d), 16, 16, None, None, None) == INVALID
     assert lib.sra_count_live_pairs(None, buf) == INVALID
+
+
+def test_invalid_rope_arguments_rejected(lib):
+    R = lib.sra_rope_permute
+
+    def rope(d=None, x=FAKE, y=FAKE2, pos=None, base=10000.0):
+        return R(ctypes.byref(d if d is not None else desc()), x, y, pos, base, None)
+
+    assert R(None, FAKE, FAKE2, None, 10000.0, None) == INVALID
+    assert rope(desc(seq=63)) == INVALID                   # seq % n_dev
+    assert rope(desc(order=3)) == INVALID
+    assert rope(desc(dtype=5)) == INVALID
+    assert rope(desc(heads=0)) == INVALID
+    assert rope(desc(head_dim=12)) == UNSUPPORTED          # not a multiple of 8
+    assert rope(desc(head_dim=264)) == UNSUPPORTED         # beyond 256
+    assert b"head_dim" in lib.sra_last_error()
+    assert rope(base=1.0) == INVALID
+    assert rope(base=float("inf")) == INVALID
+    assert rope(base=float("nan")) == INVALID
+    assert rope(x=None) == INVALID
+    assert rope(y=ctypes.c_void_p((1 << 30) + 8)) == INVALID                 # misaligned
+    assert rope(pos=ctypes.c_void_p((1 << 30) + 4)) == INVALID               # misaligned positions
+    # striped device layout: rows move, so x and y must not overlap at all
+    assert rope(desc(layout=oracle.STRIPED), y=FAKE) == INVALID
+    assert rope(desc(layout=oracle.STRIPED), y=ctypes.c_void_p((1 << 20) + 4096)) == INVALID
+    assert b"overlap" in lib.sra_last_error()
