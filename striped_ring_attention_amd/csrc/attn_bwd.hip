@@ -44,7 +44,6 @@ namespace {
 using namespace kc;
 
 constexpr int D = 128;
-constexpr int KP = D + 8;     // row-major tile pitch in LDS (elements)
 
 // ------------------------------------------------------------------ Delta --
 
@@ -77,30 +76,45 @@ __global__ void __launch_bounds__(256) bwd_delta(const bf16* __restrict__ o, con
 
 // -------------------------------------------------------------------- dQ --
 
-constexpr int QBM = 128;          // query rows per workgroup
+constexpr int QBM = 256;          // query rows per workgroup (8 waves x 32)
 constexpr int QBN = 64;           // keys per tile
-constexpr int QVP = QBN + 8;      // K^T tile pitch (elements)
+constexpr int DQ_NT = 512;
+constexpr int DQ_NS = 4;          // LDS stages, tiles loaded three ahead
+constexpr int kWaitVm8 = 0x0F78;  // vmcnt(8): the two newest tiles (4 loads each per wave) may be in flight
+
+// K and V tiles are stored row-major with 256-byte rows and no padding (they
+// are loaded straight into LDS); 16-byte chunk c of key row r sits in slot
+// c ^ swz(r), swz(r) = 4 (r % 4) + (r / 4) % 4, which keeps both the row
+// reads of the S and dP products and the transposing K^T reads of the dQ
+// product free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 struct __align__(16) SmemDq {
-    bf16 kr[QBN * KP];    // K tile, row-major
-    bf16 kt[D * QVP];     // K tile, dimension-major, permuted key order
-    bf16 vr[QBN * KP];    // V tile, row-major
+    bf16 k[DQ_NS][QBN * D];   // K tiles
+    bf16 v[DQ_NS][QBN * D];   // V tiles
 };
 
-__global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
+// A workgroup owns 256 query rows (8 waves x 32) of one device and walks the
+// (round, 64-key tile) pairs in ring order. Per 32-key block: S^T = K Q^T
+// and dP^T = V dO^T on MFMA (Q^T and dO^T held in registers, K and V rows
+// from LDS), dS^T = P^T (dP^T - Delta) scale with P^T = 2^(S^T scale log2 e -
+// LSE log2 e), then dQ^T += K^T dS^T with K^T read transposed from the
+// row-major K tile through ds_read_b64_tr_b16. Waves 0-3 load K tiles and
+// waves 4-7 V tiles straight into a 4-stage LDS ring, three tiles ahead;
+// one barrier per tile.
+__global__ void __launch_bounds__(DQ_NT, 1) bwd_dq(BwdArgs a) {
     __shared__ SmemDq sm;
     const int L = (int)a.L;
     const int64_t nqt = (a.L + QBM - 1) / QBM;
     const WorkItem wi = decode_work(nqt, a.B, a.H, a.N, 0);
     const int d = (int)wi.d;
-    const int qt = (int)uniform_i64(nqt - 1 - wi.heavy_rank);
+    const int qt = (int)uniform_i64(nqt - 1 - wi.heavy_rank);   // late query tiles meet the most keys
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;
     const int j0 = qt * QBM;
     const int j1 = min(j0 + QBM, L);
 
-    const int rs = (int)(a.H * D);
-    const int row_bytes = rs * 2;
+    const int row_bytes = (int)(a.H * D) * 2;
     // Device t's j-th token sits at slot mem_slot(t, j); consecutive tokens of
     // a device are rstride bytes apart.
     const bool strided = a.strided != 0;
@@ -125,7 +139,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     const int jw_last = min(jw0 + 31, L - 1);
     const int64_t row = (wi.b * a.S + mem_slot(strided, a.N, a.L, d, min(j, L - 1))) * a.H + wi.h;
 
-    // Q^T and dO^T operands (lane: query c32, dims kk*16 + 8*h2 .. +7).
+    // Q^T and dO^T operands (lane: query c32, dims kk*16 + 8*h2 .. +7) and the
+    // row statistics; awaited together with the first tiles below.
     bf16x8 qreg[8], doreg[8];
     {
         const bf16x8* qp = (const bf16x8*)((const bf16*)a.q + row * D) + h2;
@@ -138,9 +153,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     }
     const int64_t srow = (wi.b * a.H + wi.h) * a.S + mem_slot(strided, a.N, a.L, d, min(j, L - 1));
     const float2 st2 = *(const float2*)(a.stats + 2 * srow);
-    const float lse_l2 = row_ok ? st2.x : 0.f;
-    const float dlt = row_ok ? st2.y : 0.f;
-    __builtin_amdgcn_s_waitcnt(0);   // row operands land before any tile load is issued
 
     f32x16 dqacc[4];
 #pragma unroll
@@ -148,42 +160,42 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
     const float sl = a.scale_log2;
     const float scale = a.scale;
 
-    // Tile staging: K as (key quad kq, 8-dim chunk dc) -- four keys x 16 bytes
-    // per thread, written row-major and transposed; V as (key row kr, 32-dim
-    // chunk kc) -- four 16-byte loads per thread, written row-major.
-    const int kq = tid & 15, dc = tid >> 4;
-    const int kr = tid >> 2, kcc = tid & 3;
-    const int k_voff = 4 * kq * rstride + dc * 16;
-    const int v_voff = kr * rstride + kcc * 64;
-    const int kt_col = 16 * (kq >> 2) + 4 * ((kq & 1) * 2 + ((kq >> 1) & 1));
-    u32x4 kst[4], vst[4];
-
-    auto load_tile = [&](int s, int kt, bool valid) {
+    // Loads: group 0 (waves 0-3) loads K tiles, group 1 V tiles; wave wg of a
+    // group issues four instructions per tile, instruction q covering key rows
+    // 4 wg + 16 q .. +3. Lane l writes row 4 wg + 16 q + l/16, LDS slot l % 16,
+    // loading the chunk that slot holds (for these rows swz = 4 (l/16) + wg).
+    // Each tile gets its own buffer resource (base at the tile's first row,
+    // size cut to what is left of the slab), so rows past the slab end are not
+    // read.
+    const int grp = w >> 2, wg = w & 3;
+    const int ld_voff = (4 * wg + (lane >> 4)) * rstride + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | wg));
+    const int ld_step = 16 * rstride;
+    const uint64_t ld_head = uniform_u64(grp == 0 ? k_head : v_head);
+    const uint32_t ld_lds0 = lds_addr(grp == 0 ? &sm.k[0][0] : &sm.v[0][0]) + 1024 * wg;
+    auto load_tile = [&](int s, int kt, bool valid, int stage) {
         const int64_t tile_off = (int64_t)kt * QBN * rstride;
         const int64_t left64 = span_bytes - tile_off;
         const int left = (valid && left64 > 0) ? (int)min(left64, (int64_t)QBN * rstride) : 0;
-        const uint64_t so = slot_bytes(s) + (uint64_t)tile_off;
-        const __amdgpu_buffer_rsrc_t krs = slab_rsrc((const void*)(k_head + so), left);
-        const __amdgpu_buffer_rsrc_t vrs = slab_rsrc((const void*)(v_head + so), left);
+        const i32x4 rsrc = raw_rsrc(ld_head + slot_bytes(s) + (uint64_t)tile_off, left);
+        const uint32_t dst = ld_lds0 + stage * (QBN * D * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kst[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_voff + i * rstride, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vst[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff + 16 * i, 0, 0);
+        for (int q = 0; q < 4; ++q) load_lds_b128(rsrc, ld_voff + q * ld_step, dst + 4096 * q);
     };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)&sm.kr[(4 * kq + i) * KP + 8 * dc] = kst[i];
-        bf16* ktd = &sm.kt[(8 * dc) * QVP + kt_col];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint2 lo = {pack_lo(kst[0][p], kst[1][p]), pack_lo(kst[2][p], kst[3][p])};
-            uint2 hi = {pack_hi(kst[0][p], kst[1][p]), pack_hi(kst[2][p], kst[3][p])};
-            *(uint2*)(ktd + (2 * p) * QVP) = lo;
-            *(uint2*)(ktd + (2 * p + 1) * QVP) = hi;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)&sm.vr[kr * KP + kcc * 32 + 8 * i] = vst[i];
+
+    // Transposing-read addressing for K^T: lane (g = l / 16, i = l % 16) names
+    // key row 16 kk2 + 8 rd + 4 (g / 2) + i / 4 of a 32-key block, dims
+    // 32 db + 16 (g % 2) + 4 (i % 4) .. +3, so lane l collects dim 32 db + l % 32
+    // of keys 16 kk2 + 4 h2 + 0..3 and 16 kk2 + 8 + 4 h2 + 0..3 -- the keys its
+    // dS^T registers hold. The swizzle of such a row does not depend on the
+    // block or kk2.
+    const int tg = lane >> 4, tj = lane & 15;
+    const int tr_row = 4 * (tg >> 1) + (tj >> 2);
+    const int tr_c = 2 * (tg & 1) + ((tj & 3) >> 1);
+    auto tr_off = [&](int rd, int db) {
+        const int r = 8 * rd + tr_row;
+        return r * D + 8 * ((4 * db + tr_c) ^ swz(r)) + 4 * (tj & 1);
     };
+    auto row_off = [&](int kk) { return c32 * D + 8 * ((2 * kk + h2) ^ swz(c32)); };
 
     // Tile cursor (round, key tile), in ring order.
     int cr = 0, ck = 0, cnt = tiles_of(0);
@@ -193,19 +205,41 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
             k = 0;
             nt = tiles_of(r);
         }
+        r = __builtin_amdgcn_readfirstlane(r);
+        k = __builtin_amdgcn_readfirstlane(k);
+        nt = __builtin_amdgcn_readfirstlane(nt);
     };
     settle(cr, ck, cnt);
     int lr = cr, lk = ck, lnt = cnt;   // loader cursor
 
-    if (n_tiles > 0) load_tile(source(lr), lk, true);
-    for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();   // every wave is done with the previous tile
-        store_tile();
-        __syncthreads();
+    // When a slab ends inside a key tile, zero the stages once (rows past the
+    // end are never loaded and must hold finite values). Then tiles 0..2.
+    if (L % QBN != 0) {
+        u32x4* z = (u32x4*)&sm;
+        for (int i = tid; i < (int)(sizeof(SmemDq) / 16); i += DQ_NT) z[i] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bar();
+    }
+#pragma unroll 1
+    for (int u = 0; u < 3; ++u) {
+        load_tile(source(lr), lk, u < n_tiles, u);
         ++lk;
         settle(lr, lk, lnt);
-        load_tile(source(lr), lk, t + 1 < n_tiles);   // next tile, in flight during compute
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // Q, dO, statistics and tiles 0..2 are in
+    bar();
+    const float lse_l2 = row_ok ? st2.x : 0.f;
+    const float dlt = row_ok ? st2.y : 0.f;
 
+    for (int t = 0; t < n_tiles; ++t) {
+        // Tile t+3 into the stage of tile t-1 (every wave finished it before
+        // the barrier that ended step t-1).
+        load_tile(source(lr), lk, t + 3 < n_tiles, (t + 3) & (DQ_NS - 1));
+        ++lk;
+        settle(lr, lk, lnt);
+
+        const bf16* ks = sm.k[t & (DQ_NS - 1)];
+        const bf16* vs = sm.v[t & (DQ_NS - 1)];
         const int delta = delta_of(cr);
         const int k0 = ck * QBN;
         const int kw_end = wave_live ? live32(jw_last, delta, L) : 0;
@@ -214,15 +248,33 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (k0 + 32 * kb >= kw_end) continue;   // no live key for this wave
-            const bf16* ks = &sm.kr[(32 * kb + c32) * KP + 8 * h2];
-            const bf16* vs = &sm.vr[(32 * kb + c32) * KP + 8 * h2];
-            f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)ks, qreg[0], f32x16{}, 0, 0, 0);
-            f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)vs, doreg[0], f32x16{}, 0, 0, 0);
+            const bf16* kb_s = ks + 32 * kb * D;
+            const bf16* vb_s = vs + 32 * kb * D;
+            bf16x8 kr[8], vr[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                kr[kk] = *(const bf16x8*)&kb_s[row_off(kk)];
+                vr[kk] = *(const bf16x8*)&vb_s[row_off(kk)];
+            }
+            f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[0], qreg[0], f32x16{}, 0, 0, 0);
+            f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[0], doreg[0], f32x16{}, 0, 0, 0);
 #pragma unroll
             for (int kk = 1; kk < 8; ++kk) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ks + 16 * kk), qreg[kk], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vs + 16 * kk), doreg[kk], dp, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk], qreg[kk], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[kk], doreg[kk], dp, 0, 0, 0);
             }
+            // K^T operands of this block, read while the S and dP MFMAs run.
+            bf16x8 kt[2][4];
+#pragma unroll
+            for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(kb_s + 16 * kk2 * D + tr_off(0, db)));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(SRA_LDS4(kb_s + 16 * kk2 * D + tr_off(1, db)));
+                    kt[kk2][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            // Accumulator element i of this lane is key k0 + 32 kb + 8 (i/4) + 4 h2 + i%4
+            // against query c32.
             if (masked) {
                 const int lim = c_row - (k0 + 32 * kb) - 4 * h2;
 #pragma unroll
@@ -236,17 +288,18 @@ __global__ void __launch_bounds__(256, 2) bwd_dq(BwdArgs a) {
                 dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dlt) * scale);
             }
 #pragma unroll
-            for (int kk2 = 0; kk2 < 2; ++kk2) {
-                const bf16* kts = &sm.kt[c32 * QVP + 32 * kb + 16 * kk2 + 8 * h2];
+            for (int kk2 = 0; kk2 < 2; ++kk2)
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
-                    dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kts + db * 32 * QVP), dsb[kk2],
-                                                                       dqacc[db], 0, 0, 0);
-            }
+                    dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[kk2][db], dsb[kk2], dqacc[db], 0, 0, 0);
         }
         ++ck;
         settle(cr, ck, cnt);
+        __builtin_amdgcn_s_waitcnt(kWaitVm8);   // tile t+1 is in
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        bar();
     }
+    __builtin_amdgcn_s_waitcnt(0);   // no load may still be writing LDS when the workgroup ends
 
     if (!row_ok) return;
     bf16* dqp = (bf16*)a.dq + row * D;
@@ -275,7 +328,7 @@ hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nq = (a.L + QBM - 1) / QBM * a.H * a.N * a.B;
-    hipLaunchKernelGGL(bwd_dq, dim3((unsigned)nq), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq, dim3((unsigned)nq), dim3(DQ_NT), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_bwd_dkdv_bf16_d128(a, stream);
