@@ -73,25 +73,32 @@ def attention_rows(q, k, v, rows, scale=None):
     """Causal attention for selected original positions only (for shapes where
     the dense oracle is too slow). ``rows`` is a 1-D integer array.
 
-    Returns (O[B, len(rows), H, D], lse[B, len(rows), H]) in float64.
-    Each row i costs O(i * D) per head.
+    Returns (O[B, len(rows), H, D], lse[B, len(rows), H]) in float64. Per
+    (batch, head): the scores of all selected rows against keys 0 .. max(rows)
+    in one product, keys after a row's own position set to -inf, then the
+    row softmax and its product with V -- the definition above, row by row.
     """
     rows = np.asarray(rows, dtype=np.int64)
     B, S, H, D = q.shape
     sc = _scale(D, scale)
     o = np.zeros((B, len(rows), H, D))
     lse = np.zeros((B, len(rows), H))
-    for n, i in enumerate(rows):
-        i = int(i)
-        qi = _f64(q[:, i])              # [B, H, D]
-        kk = _f64(k[:, :i + 1])         # [B, i+1, H, D]
-        vv = _f64(v[:, :i + 1])
-        s = sc * np.einsum("bhc,bkhc->bhk", qi, kk)
-        m = s.max(axis=2, keepdims=True)
-        e = np.exp(s - m)
-        den = e.sum(axis=2, keepdims=True)
-        o[:, n] = np.einsum("bhk,bkhc->bhc", e, vv) / den
-        lse[:, n] = (m + np.log(den))[..., 0]
+    if len(rows) == 0:
+        return o, lse
+    i1 = int(rows.max()) + 1
+    keys = np.arange(i1)
+    for b in range(B):
+        for h in range(H):
+            Q = _f64(q[b, rows, h])         # [R, D]
+            K = _f64(k[b, :i1, h])          # [i1, D]
+            V = _f64(v[b, :i1, h])
+            s = sc * (Q @ K.T)
+            s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            den = e.sum(axis=1, keepdims=True)
+            o[b, :, h] = (e @ V) / den
+            lse[b, :, h] = (m + np.log(den))[:, 0]
     return o, lse
 
 

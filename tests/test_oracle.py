@@ -135,6 +135,20 @@ def test_single_device_matches_torch_sdpa_fp64():
     np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
 
 
+def _pin_rows(mod):
+    q, k, v = (rand((1, 21, 2, 3), s) for s in (21, 22, 23))
+    rows = np.array([0, 1, 7, 20])
+    o, lse = mod.attention_rows(q, k, v, rows)
+    for h in range(2):
+        O, LSE = bf_causal(q[0, :, h].tolist(), k[0, :, h].tolist(), v[0, :, h].tolist(), 1.0 / math.sqrt(3))
+        np.testing.assert_allclose(o[0, :, h], np.array(O)[rows], atol=1e-12)
+        np.testing.assert_allclose(lse[0, :, h], np.array(LSE)[rows], atol=1e-12)
+
+
+def test_attention_rows_brute_force():
+    _pin_rows(oracle)
+
+
 def test_attention_rows_matches_dense():
     q, k, v = (rand((2, 520, 2, 8), s) for s in (18, 19, 20))
     o, lse = oracle.dense_causal_attention(q, k, v)
@@ -582,6 +596,8 @@ MUTATIONS = [
     ("attention.py", "o[b, i0:i1, h] = (e @ V[:i1]) / den", "o[b, i0:i1, h] = (e @ K[:i1]) / den", _pin_dense),
     ("attention.py", "lse[b, i0:i1, h] = (m + np.log(den))[:, 0]", "lse[b, i0:i1, h] = (np.log(den))[:, 0]", _pin_dense),
     ("attention.py", "live = kpos[None, :] <= qpos[:, None]", "live = kpos[None, :] < qpos[:, None]", _pin_ring),
+    ("attention.py", "s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)",
+     "s = np.where(keys[None, :] < rows[:, None], s, -np.inf)", _pin_rows),
     ("attention.py", "K = k_dev[b, s_dev * L:(s_dev + 1) * L, h]", "K = k_dev[b, d * L:(d + 1) * L, h]", _pin_ring),
     ("attention.py", "o = (wa / tot)[..., None] * o_a + (wb / tot)[..., None] * o_b",
      "o = (wb / tot)[..., None] * o_a + (wa / tot)[..., None] * o_b", _pin_merge),
