@@ -99,3 +99,26 @@ def test_bwd_short_sum_rules_and_first_row(sra, short_bwd):
     # bf16 outputs: each of 8192 summed rows carries up to ~2^-9 relative rounding.
     # dQ_0 is zero up to rounding: P_00 is recomputed from the saved LSE.
     assert e1 <= 0.5 and e2 <= 0.5 and e3 <= 1e-5
+
+
+def test_bwd_reduced_very_long_ring_dense_parity(sra):
+    """The Very long ring's device count (N = 16) at a shape the dense fp64
+    oracle still finishes: S = 16,384, 2 heads, both layouts, with the
+    backward's inputs in original token order (the striped path reads each
+    device's rows in place)."""
+    S, N, H = 16384, 16, 2
+    x = rand_inputs(S, H, 4242)
+    say(f"reduced very-long backward: S={S} N={N} H={H}: oracle ...")
+    o_ref, l_ref = oracle.dense_causal_attention(x["q"], x["k"], x["v"])
+    ref = oracle.dense_causal_backward(x["q"], x["k"], x["v"], o_ref, l_ref, x["do"])
+    xg = {n: t.cuda() for n, t in x.items()}
+    for layout in LAYOUTS:
+        o, lse = sra.ring_attn_fwd(xg["q"], xg["k"], xg["v"], N, layout, schedule=sra.SCHEDULE_FUSED,
+                                   order=sra.ORDER_ORIGINAL)
+        dq, dk, dv = sra.ring_attn_bwd(xg["q"], xg["k"], xg["v"], o, lse, xg["do"], N, layout,
+                                       order=sra.ORDER_ORIGINAL)
+        torch.cuda.synchronize()
+        e_f = [float(np.abs(np64(o) - o_ref).max()), float(np.abs(np64(lse) - l_ref).max())]
+        errs = [float(np.abs(np64(g) - r).max()) for g, r in zip((dq, dk, dv), ref)]
+        say(f"  layout={layout}: O {e_f[0]:.3g} LSE {e_f[1]:.3g} dq {errs[0]:.3g} dk {errs[1]:.3g} dv {errs[2]:.3g}")
+        assert max(e_f + errs) <= 2e-2, (e_f, errs)
