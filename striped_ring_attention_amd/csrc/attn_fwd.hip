@@ -110,10 +110,19 @@ struct TileCursor {
 
 struct RoundGeom {
     int L, N, layout, d, j_last, r_hi;
+    // Enter round c.r. 32-bit scalar arithmetic only: s = (d - r) mod N
+    // without a division (0 <= d, r < N). The shift is only ever used through
+    // live32(j, delta, L) with 0 <= j < L, so with a contiguous layout it is
+    // reduced to what that sees: a source after d has no live key for any
+    // query (-L-1), one before d has all of them (L+1), and s = d is the
+    // causal block (1).
     __device__ __forceinline__ void enter(TileCursor& c) const {
-        c.s = __builtin_amdgcn_readfirstlane((d - c.r + N) % N);
-        c.delta = __builtin_amdgcn_readfirstlane(clamp_delta(live_delta(layout, N, L, d, c.s), L));
-        c.nt = __builtin_amdgcn_readfirstlane((live32(j_last, c.delta, L) + BN - 1) / BN);
+        int s = d - c.r;
+        if (s < 0) s += N;
+        const int dl = layout == 1 ? (s <= d ? 1 : 0) : (s == d ? 1 : (s < d ? L + 1 : -L - 1));
+        c.s = __builtin_amdgcn_readfirstlane(s);
+        c.delta = __builtin_amdgcn_readfirstlane(dl);
+        c.nt = __builtin_amdgcn_readfirstlane((int)((unsigned)(live32(j_last, c.delta, L) + BN - 1) / BN));
         c.kt = 0;
     }
     // Move to the first tile at or after the cursor's position.
@@ -377,23 +386,27 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     // of group 1 -- both before the barrier that opens the loading group's
     // Y(t). Tile t+1's K is first read in X(t+1) and its V in X(t+2), both
     // after the barrier that closes the loading group's Y(t).
+    // The cursor of the next step and whether this wave is active in it are
+    // worked out in phase Y, which has slack, so that phase X starts straight
+    // with its LDS reads and MFMAs.
     TileCursor cur = c0;
     bool act_prev = false;
+    bool act = n_tiles > 0 && wave_active(cur);
     if (grp == 1) bar();   // group 1 sits out the first phase
     for (int t = 0;; ++t) {
-        const bool act = t < n_tiles && wave_active(cur);
         if (act_prev) compute_pv((t - 1) & (NS - 1));
         if (act) compute_s(t & (NS - 1));
         if (t == n_tiles) break;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         bar();
         if (act) softmax(cur);
+        act_prev = act;
+        geo.advance(cur);
+        act = t + 1 < n_tiles && wave_active(cur);
         __builtin_amdgcn_s_waitcnt(kWaitVm4);
         load_tile(ld, t + 3 < n_tiles, (t + 3) & (NS - 1));
         geo.advance(ld);
         bar();
-        act_prev = act;
-        geo.advance(cur);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     if (grp == 0) bar();   // match group 1's extra first-phase barrier
