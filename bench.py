@@ -47,10 +47,10 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # on the stripe-permute copy kernel of known size; filled in from the counter
 # summary under profiles/ and valid only for the kernel sources it was taken on.
 TRAFFIC = {"workload": "short", "order": "original",
-           "kernel_sources_sha256": "a428794dc398d9c6749e18208e285b4a08e6f562029bfa431d743a789411d1a1",
-           "bytes_per_launch": 926078824,
-           "fetch_bytes_per_launch": 890409232, "write_bytes_per_launch": 35669592,
-           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99977}}
+           "kernel_sources_sha256": "b5b14933428c808390c3302438a128aae41484e704636457dfa04473513809bf",
+           "bytes_per_launch": 928368752,
+           "fetch_bytes_per_launch": 892697376, "write_bytes_per_launch": 35671376,
+           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99982}}
 
 
 def parse():

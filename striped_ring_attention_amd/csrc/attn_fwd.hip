@@ -32,7 +32,8 @@
 //    does not depend on the offset; it only bounds p <= 256), so the
 //    64-register rescale of O is rare.
 //  * K and V tiles go from HBM straight into a 4-stage LDS ring
-//    (buffer_load ... lds, no register staging), three tiles ahead of use;
+//    (buffer_load ... lds, no register staging), K three tiles and V two
+//    tiles ahead of the step that first reads them;
 //    16-byte chunks are XOR-swizzled per row so both MFMA operand read
 //    patterns are bank-conflict-free.
 #include "kernel_common.h"
@@ -144,13 +145,15 @@ struct RoundGeom {
 //   running (O, max, sum) across rounds, which is the log-sum-exp merge of
 //   the per-round partial results, and the epilogue writes the output.
 //
-// Schedule ("ping-pong"): the two groups of 4 wavefronts run the same tile
-// sequence one phase apart. In phase X(t) a wave issues its MFMAs: O += P V
-// for tile t-1, then S = K Q^T for tile t. In phase Y(t) it runs the softmax
-// of tile t on the vector ALU. Group 1 starts one phase late, and waves w and
-// w+4 share a SIMD, so on every SIMD one wave is in X while the other is in
-// Y; a workgroup barrier separates consecutive phases. In its Y(t) group 0
-// starts the loads of K(t+3) and group 1 those of V(t+3).
+// Schedule: the tile sequence runs in steps, one workgroup barrier per step.
+// X(t) is a wave's MFMA work -- O += P V for tile t-1, then S = K Q^T for
+// tile t -- and Y(t) its softmax of tile t on the vector ALU. In step t group
+// 0 runs X(t) then Y(t), and group 1 runs Y(t-1) then X(t). Waves w and w+4
+// share a SIMD, so every step starts with one wave of each SIMD on the MFMA
+// unit and the other on the vector ALU, and the two swap roles half-way; the
+// wave in X runs at raised issue priority. Group 0 loads K three tiles ahead
+// (in Y(t), K(t+3)), group 1 V two tiles ahead (at the start of its step,
+// V(t+2)).
 template <bool kFused>
 __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int flags) {
     __shared__ SmemBf16 sm;
@@ -362,11 +365,14 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     geo.advance(c1);
     TileCursor c2 = c1;
     geo.advance(c2);
-    TileCursor ld = c2;
+    // Group 0 loads K three tiles ahead, group 1 V two tiles ahead.
+    TileCursor ld = c1;
+    if (grp == 0) geo.advance(ld);
     geo.advance(ld);
 
     // Zero the stages once (rows past a slab end are never loaded), then put
-    // tiles 0, 1, 2 in flight and wait for tile 0.
+    // K(0..2) and V(0..1) in flight and wait for K(0). V(0) is first read in
+    // step 1; group 1 waits for it in step 0.
     {
         u32x4* z = (u32x4*)&sm;
         for (int i = tid; i < (int)(sizeof(SmemBf16) / 16); i += NT) z[i] = u32x4{0u, 0u, 0u, 0u};
@@ -375,41 +381,58 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     }
     load_tile(c0, n_tiles > 0, 0);
     load_tile(c1, n_tiles > 1, 1);
-    load_tile(c2, n_tiles > 2, 2);
-    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    if (grp == 0) {
+        load_tile(c2, n_tiles > 2, 2);
+        __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    }
     bar();
 
-    // Main loop. Phase X(t): MFMAs (P V of tile t-1, then S of tile t).
-    // Phase Y(t): softmax of tile t; the group waits for its part of tile t+1
-    // and starts the loads of its part of tile t+3 into the stage of tile t-1.
-    // Stage reuse: K(t-1) was last read in X(t-1) of group 1, V(t-1) in X(t)
-    // of group 1 -- both before the barrier that opens the loading group's
-    // Y(t). Tile t+1's K is first read in X(t+1) and its V in X(t+2), both
-    // after the barrier that closes the loading group's Y(t).
-    // The cursor of the next step and whether this wave is active in it are
-    // worked out in phase Y, which has slack, so that phase X starts straight
-    // with its LDS reads and MFMAs.
+    // Main loop, step t (tile t's K is read in step t, its V in step t+1).
+    // Loads: group 0 starts K(t+3) into the stage of tile t-1, whose K was
+    // last read in step t-1; group 1 starts V(t+2) into the stage of tile
+    // t-2, whose V was last read in step t-1. Before that each waits for the
+    // oldest of its two tiles in flight (K(t+1), V(t)), which the next step
+    // reads. Every wave drains its LDS reads before the step's barrier, so a
+    // stage is never refilled while read, and a tile is complete before the
+    // barrier that precedes its first use. The cursor of the next tile and
+    // whether this wave is active in it are worked out next to the softmax,
+    // off the MFMA work.
     TileCursor cur = c0;
     bool act_prev = false;
     bool act = n_tiles > 0 && wave_active(cur);
-    if (grp == 1) bar();   // group 1 sits out the first phase
     for (int t = 0;; ++t) {
+        if (grp == 1) {
+            if (t > 0) {
+                if (act_prev) softmax(cur);
+                geo.advance(cur);
+                act = t < n_tiles && wave_active(cur);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVm4);
+            load_tile(ld, t + 2 < n_tiles, (t + 2) & (NS - 1));
+            geo.advance(ld);
+        }
+        __builtin_amdgcn_s_setprio(1);
         if (act_prev) compute_pv((t - 1) & (NS - 1));
         if (act) compute_s(t & (NS - 1));
+        __builtin_amdgcn_s_setprio(0);
+        if (grp == 0) {
+            if (t < n_tiles) {
+                if (act) softmax(cur);
+                act_prev = act;
+                geo.advance(cur);
+                act = t + 1 < n_tiles && wave_active(cur);
+                __builtin_amdgcn_s_waitcnt(kWaitVm4);
+                load_tile(ld, t + 3 < n_tiles, (t + 3) & (NS - 1));
+                geo.advance(ld);
+            }
+        } else {
+            act_prev = act;
+        }
         if (t == n_tiles) break;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         bar();
-        if (act) softmax(cur);
-        act_prev = act;
-        geo.advance(cur);
-        act = t + 1 < n_tiles && wave_active(cur);
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);
-        load_tile(ld, t + 3 < n_tiles, (t + 3) & (NS - 1));
-        geo.advance(ld);
-        bar();
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    if (grp == 0) bar();   // match group 1's extra first-phase barrier
     __builtin_amdgcn_s_waitcnt(0);   // no load may still be writing LDS when the workgroup ends
 
     // Finish the row: l = both halves' sums; O = O / l; lse in natural log.
