@@ -110,6 +110,23 @@ def cpu_baseline(x, seconds):
                                         f"host has {cores} cores available"}
 
 
+def queried_peak_bf16(torch):
+    """Dense bf16 MFMA peak from the device's own properties: compute units x
+    4 SIMDs x 1,024 bf16 flop per clock (one 32x32x16 MFMA per 32 cycles) x the
+    peak engine clock that HIP reports. Reported next to the published figure."""
+    import ctypes
+    dev = torch.cuda.current_device()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    khz = ctypes.c_int(0)
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, dev) != 0:   # 5: hipDeviceAttributeClockRate (kHz)
+            return None
+    except OSError:
+        return None
+    return {"TFLOP/s": cus * 4096 * khz.value * 1e3 / 1e12, "compute_units": cus, "clock_mhz": khz.value / 1e3}
+
+
 def kernel_source_digest():
     """sha256 over the sources the forward ring kernel is compiled from."""
     h = hashlib.sha256()
@@ -413,7 +430,8 @@ def main():
                      "launches_per_step": nl, "avg_launch_ms": attn_ms / nl,
                      "step_kernel_ms_median_min_max": [statistics.median(ring_ms_steps), min(ring_ms_steps),
                                                        max(ring_ms_steps)],
-                     "flops_per_launch": flops_per_launch},
+                     "flops_per_launch": flops_per_launch,
+                     "peak_queried": queried_peak_bf16(torch)},
         "imbalance": imb, "permutation": perm, "model_input": model_input, "compare": compare, "backward": backward,
         "critical_path": critical,
         "wall_s_timed": wall,
