@@ -113,7 +113,8 @@ def test_round_partials_fp32_d128_ragged(sra):
     _partials_case(sra, 3 * 70, 3, 2, 128, torch.float32, 2)
 
 
-@pytest.mark.parametrize("S,N,H", [(1024, 2, 2), (8 * 200, 8, 2), (512, 4, 3), (16, 16, 1), (130, 1, 2)])
+@pytest.mark.parametrize("S,N,H", [(1024, 2, 2), (8 * 200, 8, 2), (512, 4, 3), (16, 16, 1), (130, 1, 2),
+                                   (64, 1, 1), (128, 1, 1)])
 def test_round_partials_bf16(sra, S, N, H):
     _partials_case(sra, S, N, H, 128, torch.bfloat16, 3 + S + N)
 
@@ -289,10 +290,12 @@ def test_fwd_short_bf16_fused_dense_parity(sra, short_case, layout):
     assert (lse - l2).abs().max().item() <= 1e-4
 
 
-@pytest.mark.parametrize("S,N,H", [(8 * 200, 8, 2), (1024, 1, 2), (16, 16, 1), (4 * 300, 4, 3)])
+@pytest.mark.parametrize("S,N,H", [(8 * 200, 8, 2), (1024, 1, 2), (16, 16, 1), (4 * 300, 4, 3),
+                                   (64, 1, 1), (128, 1, 2), (192, 1, 1), (2 * 96, 2, 1)])
 def test_fwd_fused_small_dense_parity(sra, S, N, H):
     """Ragged shards (L not a multiple of the 256 x 64 tile), one device, one
-    token per device; both layouts."""
+    token per device, and workgroups with one, two or three key tiles in all
+    (the first and last steps of both wave groups); both layouts."""
     g = torch.Generator().manual_seed(S + N + H)
     x = {n: (torch.randn((1, S, H, 128), generator=g) * 0.5).to(torch.bfloat16) for n in ("q", "k", "v")}
     o_ref, l_ref = oracle.dense_causal_attention(x["q"], x["k"], x["v"])
