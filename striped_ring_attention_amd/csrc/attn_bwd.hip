@@ -17,14 +17,13 @@
 // empty tiles and masking only partial ones.
 //
 //  * bwd_delta:  Delta = rowsum(dO * O) in fp32.
-//  * bwd_dq:     a workgroup owns 128 query rows (4 waves x 32) and walks
+//  * bwd_dq:     a workgroup owns 256 query rows (8 waves x 32) and walks
 //                the (round, 64-key tile) pairs in ring order. Per 32-key
 //                block: S^T = K Q^T and dP^T = V dO^T on MFMA (Q^T and dO^T
 //                held in registers, K and V row-major in LDS), then
 //                dS^T = P^T (dP^T - Delta) scale, and dQ^T += K^T dS^T with
-//                K^T read from a dimension-major LDS copy whose 16-key groups
-//                are ordered [0-3, 8-11, 4-7, 12-15] (the order in which a
-//                lane's accumulator registers hold keys).
+//                K^T read from the row-major K tile by transposing LDS reads
+//                (ds_read_b64_tr_b16).
 //  * bwd_dkdv:   a workgroup owns 128 keys (4 groups x 32) of one source
 //                device and walks the 32-row query tiles of every device that
 //                meets the block, round by round. Two waves per 32-key group:
