@@ -355,7 +355,31 @@ def main():
     model_input = {"rope_permute_qk_ms": r_ms, "rope_permute_GBps": r_bytes / (r_ms * 1e-3) / 1e9,
                    "rope_permute_cold_GBps": r_bytes / (rc_ms * 1e-3) / 1e9, "hbm_peak_GBps": PEAK_HBM_GBS,
                    "note": "Q and K rotated at original positions and gathered into the layout; not part of value"}
-    del flush
+
+    # Unfused log-sum-exp merge of one round's fp32 partial into the running
+    # (O, LSE): per row (2 Dh + 2) fp32 read and (Dh + 1) written. The driver
+    # fuses this into the round kernel's epilogue; the standalone kernel is the
+    # unfused form.
+    g = torch.Generator(device=dev).manual_seed(7)
+    m_oa = torch.randn((B, S, H, D), generator=g, device=dev)
+    m_op = torch.randn((B, S, H, D), generator=g, device=dev)
+    m_la = torch.randn((B, S, H), generator=g, device=dev)
+    m_lp = torch.randn((B, S, H), generator=g, device=dev)
+    sra.lse_merge(m_oa, m_la, m_op, m_lp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        sra.lse_merge(m_oa, m_la, m_op, m_lp)
+    e1.record()
+    torch.cuda.synchronize()
+    m_ms = e0.elapsed_time(e1) / 10
+    m_bytes = B * S * H * (3 * D + 3) * 4
+    mc_ms = cold_ms(lambda: sra.lse_merge(m_oa, m_la, m_op, m_lp))
+    merge = {"lse_merge_ms": m_ms, "lse_merge_GBps": m_bytes / (m_ms * 1e-3) / 1e9,
+             "lse_merge_cold_GBps": m_bytes / (mc_ms * 1e-3) / 1e9, "bytes": m_bytes, "hbm_peak_GBps": PEAK_HBM_GBS,
+             "note": "standalone unfused merge of one fp32 partial, rows B*S*H; not part of value"}
+    del flush, m_oa, m_op, m_la, m_lp
 
     # Imbalance: host census at 128x128 tiles and at the kernel's own tiles; device counters.
     tq, tk = sra.kernel_tiles(torch.bfloat16, D)
@@ -432,7 +456,7 @@ def main():
                                                        max(ring_ms_steps)],
                      "flops_per_launch": flops_per_launch,
                      "peak_queried": queried_peak_bf16(torch)},
-        "imbalance": imb, "permutation": perm, "model_input": model_input, "compare": compare, "backward": backward,
+        "imbalance": imb, "permutation": perm, "model_input": model_input, "lse_merge": merge, "compare": compare, "backward": backward,
         "critical_path": critical,
         "wall_s_timed": wall,
     }
