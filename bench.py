@@ -47,10 +47,10 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # on the stripe-permute copy kernel of known size; filled in from the counter
 # summary under profiles/ and valid only for the kernel sources it was taken on.
 TRAFFIC = {"workload": "short", "order": "original",
-           "kernel_sources_sha256": "b5b14933428c808390c3302438a128aae41484e704636457dfa04473513809bf",
-           "bytes_per_launch": 928368752,
-           "fetch_bytes_per_launch": 892697376, "write_bytes_per_launch": 35671376,
-           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99982}}
+           "kernel_sources_sha256": "1007c337c5f63b4c85b4792b456e85bba7d1d92189ed4fb7ef41a5ed3c0220ca",
+           "bytes_per_launch": 925915804,
+           "fetch_bytes_per_launch": 890252699, "write_bytes_per_launch": 35663105,
+           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99959}}
 
 
 def parse():

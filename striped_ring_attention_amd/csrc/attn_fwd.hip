@@ -314,14 +314,18 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     // fp32 row sum, bf16 P^T operands.
     auto softmax = [&](const TileCursor& c) {
         const int k0 = c.kt * BN;
-        if (k0 + BN > live32(jw0, c.delta, L)) {
+        const int live_first = live32(jw0, c.delta, L);   // fewest live keys of the wave's rows
+        if (k0 + BN > live_first) {
             const int lim = (row_ok ? live32(j, c.delta, L) : 0) - k0 - 4 * h2;
+            // The first 32 keys need no mask when every row of the wave has them.
+            if (k0 + 32 > live_first) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int off = 8 * (i >> 2) + (i & 3);
-                if (off >= lim) sacc[0][i] = -INFINITY;
-                if (off + 32 >= lim) sacc[1][i] = -INFINITY;
+                for (int i = 0; i < 16; ++i)
+                    if (8 * (i >> 2) + (i & 3) >= lim) sacc[0][i] = -INFINITY;
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (8 * (i >> 2) + (i & 3) + 32 >= lim) sacc[1][i] = -INFINITY;
         }
         float mx = fmaxf(fmaxf(sacc[0][0], sacc[1][0]), sacc[0][1]);
 #pragma unroll
@@ -339,13 +343,13 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
             m_run = m_new;
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float ls0 = 0.f, ls1 = 0.f;
+        float ls0, ls1;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], sl, -m_use));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], sl, -m_use));
-            ls0 += p0;
-            ls1 += p1;
+            ls0 = i == 0 ? p0 : ls0 + p0;
+            ls1 = i == 0 ? p1 : ls1 + p1;
             pop[0][i >> 3][i & 7] = (bf16)p0;
             pop[1][i >> 3][i & 7] = (bf16)p1;
         }
