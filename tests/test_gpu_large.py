@@ -99,6 +99,46 @@ def test_long_forward_self_match_all_rows(sra, long_inputs):
     assert err <= 2e-2
 
 
+def _unit_rows(w, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    u = torch.randn((1, w["seq"], w["heads"], w["head_dim"]), generator=g, device="cuda")
+    return u / u.norm(dim=-1, keepdim=True)
+
+
+@pytest.mark.parametrize("layout,schedule", [(oracle.STRIPED, 1), (oracle.CONTIGUOUS, 0)])
+def test_long_forward_previous_match_all_rows(sra, long_inputs, layout, schedule):
+    """Q_i = c * U_(i-1), K = c * U (row 0 matches itself): the previous key
+    scores 64 and dominates, so O_i = V_(i-1) on every row and head -- the key
+    just before the diagonal is visible for every device pair and round."""
+    w = WORKLOADS["long"]
+    c = math.sqrt(64.0 * math.sqrt(w["head_dim"]))
+    k = (c * _unit_rows(w, 34)).to(torch.bfloat16)
+    q = torch.cat([k[:, :1], k[:, :-1]], dim=1).contiguous()
+    v = long_inputs["v"]
+    o, lse = forward(sra, q, k, v, w["n_dev"], layout, schedule)
+    want = torch.cat([v[:, :1], v[:, :-1]], dim=1)
+    err = (o.float() - want.float()).abs().max().item()
+    say(f"long previous-match layout={layout}: max |O_i - V_(i-1)| {err:.3g}")
+    assert err <= 2e-2
+
+
+def test_long_forward_future_key_masked_all_rows(sra, long_inputs):
+    """Q_i = c * U_(i+1): the matching key is one position in the future and
+    must stay masked, so O_i is a mix of past values unrelated to V_(i+1)
+    (cosine well below 0.9 on every row and head; a leaked key gives ~1)."""
+    w = WORKLOADS["long"]
+    c = math.sqrt(64.0 * math.sqrt(w["head_dim"]))
+    k = (c * _unit_rows(w, 35)).to(torch.bfloat16)
+    q = torch.cat([k[:, 1:], k[:, -1:]], dim=1).contiguous()
+    v = long_inputs["v"]
+    o, _ = forward(sra, q, k, v, w["n_dev"], oracle.STRIPED, 1)
+    nxt = v[:, 1:].float()
+    cos = torch.nn.functional.cosine_similarity(o[:, :-1].float(), nxt, dim=-1)
+    worst = cos.max().item()
+    say(f"long future-match: max cosine(O_i, V_(i+1)) {worst:.3g}")
+    assert worst < 0.9
+
+
 @pytest.fixture(scope="module")
 def very_long():
     w = WORKLOADS["very_long"]
