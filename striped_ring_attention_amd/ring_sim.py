@@ -15,7 +15,7 @@ one ring device) and timed; then
 
 where t_comm is the time to pass one K/V block to the next device, overlapped
 with the round's compute (a stated model, not a measurement: the pages name
-no interconnect and this build runs on one GPU). The projected speedup of
+no interconnect, and every simulated device runs on the same GPU). The projected speedup of
 striped over contiguous is the ratio of ring times at the same shape.
 
 Host-side functions (``critical_path``, ``ring_time``, ``kv_block_bytes``,
