@@ -4,9 +4,10 @@
 // queries attend to the K/V block of device s = (d - r) mod N (Striped
 // Attention summary page, "Summary" ¶1: K/V blocks circulate around the
 // ring). Tiles with no live pair are skipped and only partially live tiles
-// are masked ("Summary" ¶1-2: with contiguous chunks a device's work in a
-// round is all live or all masked; with stripes every device skips about
-// half in every round). The mask is the shifted causal mask k < j + delta
+// are masked ("Summary" ¶1-2: with contiguous chunks a device's block in a
+// round is either entirely live or entirely masked, while the striped layout
+// leaves every device a near-triangular, roughly half-live block in each
+// round). The mask is the shifted causal mask k < j + delta
 // (see live_delta in sra_internal.h).
 //
 // The epilogue optionally merges the round's partial result into a running
