@@ -47,10 +47,10 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # on the stripe-permute copy kernel of known size; filled in from the counter
 # summary under profiles/ and valid only for the kernel sources it was taken on.
 TRAFFIC = {"workload": "short", "order": "original",
-           "kernel_sources_sha256": "f05996e8779f1fd7ea81f0859f3e3f6b1dc6267061be082804a7b1b99bdf04ba",
-           "bytes_per_launch": 925915804,
-           "fetch_bytes_per_launch": 890252699, "write_bytes_per_launch": 35663105,
-           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99959}}
+           "kernel_sources_sha256": "c34b973a87006c107d0fc58b5cb73665df69407753a665da5a04351d2c54e1e2",
+           "bytes_per_launch": 603382955,
+           "fetch_bytes_per_launch": 565628600, "write_bytes_per_launch": 37754355,
+           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99945}}
 
 
 def parse():

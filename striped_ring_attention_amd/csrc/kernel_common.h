@@ -129,8 +129,14 @@ __device__ __forceinline__ int clamp_delta(int64_t dl, int L) {
 // the group count G = B*H*nd is a multiple of 8, XCD x owns groups
 // [x*G/8, (x+1)*G/8) -- devices of a head adjacent, so an XCD's workgroups
 // stream the same slabs through its L2 -- and hands them out heaviest tile
-// first across all of its groups, which makes the hardware's greedy dispatch
-// a longest-job-first schedule. Otherwise blocks map in plain order.
+// first, which makes the hardware's greedy dispatch a longest-job-first
+// schedule. When an XCD owns an even number of groups it hands out all tiles
+// of the first half of its groups before those of the second half (heaviest
+// first within each half): the workgroups resident at one time then read
+// fewer distinct K/V slabs (one head instead of two when an XCD owns two),
+// which raises L2 reuse, and the greedy dispatch still pairs a CU's light
+// first-half tile with a heavy second-half one. Otherwise blocks map in plain
+// order.
 struct WorkItem {
     int64_t b, h, d, heavy_rank;
 };
@@ -138,7 +144,14 @@ __device__ __forceinline__ WorkItem decode_work(int64_t ntiles, int64_t B, int64
     const int64_t G = B * H * nd;
     const int64_t i = blockIdx.x;
     int64_t qi, g;
-    if ((G & 7) == 0) {
+    if ((G & 7) == 0 && ((G >> 3) & 1) == 0) {
+        const int64_t gx = G >> 3, hx = gx >> 1;
+        const int64_t m = i >> 3;
+        const int64_t half = hx * ntiles;
+        const int64_t mm = m < half ? m : m - half;
+        qi = mm / hx;
+        g = (i & 7) * gx + (m < half ? 0 : hx) + mm % hx;
+    } else if ((G & 7) == 0) {
         const int64_t gx = G >> 3;
         const int64_t m = i >> 3;
         qi = m / gx;
