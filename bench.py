@@ -20,6 +20,10 @@ roofline = the ring attention kernel (the dominant kernel): useful flops of
          every launch in the timed region / the sum of their durations, from
          HIP events recorded on the launch stream around each launch, against
          the bf16 dense MFMA peak.
+Timing: the default warm-up and step counts depend on the workload (Short:
+300 untimed, then 300 timed steps) so that the timed region runs at the
+GPU's sustained clocks; each secondary section is preceded by ~0.15 s of the
+same work, and short kernels are timed behind queued GPU work.
 cpu_baseline = the CPU oracle (fp64 numpy dense causal attention) on a
          bounded sample of the same workload (whole sequence, heads cycled
          until about --cpu-seconds of work), rank 0 only.
@@ -56,8 +60,10 @@ TRAFFIC = {"workload": "short", "order": "original",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default per workload: about 0.1-1 s of timed GPU work)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before them (default per workload: past the clock ramp)")
     ap.add_argument("--workload", default="short")
     ap.add_argument("--layout", default="striped", choices=["striped", "contiguous"])
     ap.add_argument("--schedule", default="fused", choices=["fused", "per_round"],
@@ -73,6 +79,45 @@ def parse():
     ap.add_argument("--no-critical-path", action="store_true",
                     help="skip the per-(device, round) timing of the simulated ring")
     return ap.parse_args()
+
+
+# Default (timed steps, warm-up steps) per workload. After an idle period the
+# GPU's clocks take ~50 ms of back-to-back work to reach their sustained level
+# (a Short forward launch takes 330-380 us over its first 40 launches, then a
+# steady ~300 us for as long as it runs), so the warm-up spans >= 100 ms and
+# the timed region measures the sustained rate.
+DEFAULT_STEPS = {"short": (300, 300), "mid": (10, 4), "long": (3, 1), "very_long": (2, 1)}
+WARM_SECONDS = 0.15   # back-to-back work before each secondary timed section
+
+
+def warm(torch, fn, seconds=WARM_SECONDS):
+    """Run `fn` back to back for about `seconds`, so the section that follows
+    starts at sustained clocks instead of after host-side idle time."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    n = max(1, int(seconds / max(time.perf_counter() - t0, 1e-5)))
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+
+
+def queued_ms(torch, fn, reps=20):
+    """Mean GPU time of `fn` over `reps` back-to-back calls. The calls are
+    enqueued behind ~2.5 ms of matrix products, so the host's enqueueing of
+    short launches never leaves the GPU idle inside the timed region."""
+    pad = torch.ones((4096, 4096), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(28):
+        torch.mm(pad, pad)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def imbalance(live):
@@ -166,8 +211,8 @@ def time_backward(sra, torch, x, N, layout, ordr, fwd_step, qd, kd, vd, o_dev, l
         q, k, v, out, l, do = x["q"], x["k"], x["v"], o, lse, x["do"]
     dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
     ws = torch.empty(max(1, sra.bwd_workspace_bytes(q, N, layout)), dtype=torch.uint8, device=q.device)
-    for _ in range(2):
-        sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws, order=ordr)
+    warm(torch, lambda: sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws,
+                                          order=ordr))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     for a, b in evs:
@@ -200,6 +245,9 @@ def main():
         sys.exit(1)
     sra.load()
     w = WORKLOADS[args.workload]
+    k_def, w_def = DEFAULT_STEPS.get(args.workload, (20, 3))
+    args.steps = k_def if args.steps is None else args.steps
+    args.warmup = w_def if args.warmup is None else args.warmup
     if w["dtype"] != torch.bfloat16:
         print("bench.py times the bf16 workloads", file=sys.stderr)
         sys.exit(2)
@@ -296,7 +344,7 @@ def main():
     perm = {}
     dev_step = None
     if layout == sra.STRIPED and not dev_striped:
-        step(layout, sched, od=sra.ORDER_DEVICE)
+        warm(torch, lambda: step(layout, sched, od=sra.ORDER_DEVICE))
         d_step, d_launch, perm_ev = timed(layout, sched, K, perm=True, od=sra.ORDER_DEVICE)
         d_attn = sum(sum(p) for p in d_launch) / K
         dev_step = {"step_ms": d_step, "step_useful_TFLOPs": useful_flops / (d_step * 1e-3) / 1e12,
@@ -341,15 +389,8 @@ def main():
         sra.rope_permute(q, N, layout, out=qr_out)
         sra.rope_permute(k, N, layout, out=kr_out)
 
-    rope_qk()
-    torch.cuda.synchronize()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    for _ in range(10):
-        rope_qk()
-    r1.record()
-    torch.cuda.synchronize()
-    r_ms = r0.elapsed_time(r1) / 10
+    warm(torch, rope_qk)
+    r_ms = queued_ms(torch, rope_qk)
     r_bytes = 2 * 2 * q.numel() * q.element_size()
     rc_ms = cold_ms(rope_qk)
     model_input = {"rope_permute_qk_ms": r_ms, "rope_permute_GBps": r_bytes / (r_ms * 1e-3) / 1e9,
@@ -365,15 +406,8 @@ def main():
     m_op = torch.randn((B, S, H, D), generator=g, device=dev)
     m_la = torch.randn((B, S, H), generator=g, device=dev)
     m_lp = torch.randn((B, S, H), generator=g, device=dev)
-    sra.lse_merge(m_oa, m_la, m_op, m_lp)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        sra.lse_merge(m_oa, m_la, m_op, m_lp)
-    e1.record()
-    torch.cuda.synchronize()
-    m_ms = e0.elapsed_time(e1) / 10
+    warm(torch, lambda: sra.lse_merge(m_oa, m_la, m_op, m_lp))
+    m_ms = queued_ms(torch, lambda: sra.lse_merge(m_oa, m_la, m_op, m_lp))
     m_bytes = B * S * H * (3 * D + 3) * 4
     mc_ms = cold_ms(lambda: sra.lse_merge(m_oa, m_la, m_op, m_lp))
     merge = {"lse_merge_ms": m_ms, "lse_merge_GBps": m_bytes / (m_ms * 1e-3) / 1e9,
@@ -407,7 +441,7 @@ def main():
                                ("contiguous_fused", sra.CONTIGUOUS, sra.SCHEDULE_FUSED)):
             if lay == layout and sc == sched:
                 continue
-            step(lay, sc)
+            warm(torch, lambda: step(lay, sc))
             c_step, c_launch, _ = timed(lay, sc, K)
             c_attn = sum(sum(p) for p in c_launch) / K
             rec = {"ring_ms": c_attn, "ring_useful_TFLOPs": useful_flops / (c_attn * 1e-3) / 1e12,
@@ -423,9 +457,11 @@ def main():
     critical = None
     if not args.no_critical_path:
         from striped_ring_attention_amd import ring_sim
+        warm(torch, lambda: step(sra.CONTIGUOUS, sra.SCHEDULE_PER_ROUND))
         t_c = ring_sim.time_device_rounds(q, k, v, N, sra.CONTIGUOUS, reps=3)
         for src, dst in ((q, qd), (k, kd), (v, vd)):
             sra.stripe_permute(src, N, out=dst)
+        warm(torch, lambda: step(sra.STRIPED, sra.SCHEDULE_PER_ROUND))
         t_s = ring_sim.time_device_rounds(qd, kd, vd, N, sra.STRIPED, reps=3)
         critical = ring_sim.project(t_s, t_c, ring_sim.kv_block_bytes(B, S, H, D, N, q.element_size()))
         critical["note"] = ("one launch per (device, round) on this GPU; ring time = sum over rounds of "
