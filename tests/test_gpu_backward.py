@@ -84,6 +84,26 @@ def test_bwd_short_sampled_heads_dense_parity(sra, short_bwd):
         assert max(errs) <= 2e-2, errs
 
 
+def test_bwd_short_original_order_dense_parity(sra, short_bwd):
+    """The backward the benchmark times: Short, tensors in original token order,
+    after the fused original-order forward (all 16 heads on the GPU); the dense
+    fp64 oracle backward on two of the heads."""
+    w, x = short_bwd
+    heads = [5, 14]
+    cpu = {n: x[n][:, :, heads].cpu() for n in ("q", "k", "v", "do")}
+    o_ref, l_ref = oracle.dense_causal_attention(cpu["q"], cpu["k"], cpu["v"])
+    ref = oracle.dense_causal_backward(cpu["q"], cpu["k"], cpu["v"], o_ref, l_ref, cpu["do"])
+    for layout in LAYOUTS:
+        o, lse = sra.ring_attn_fwd(x["q"], x["k"], x["v"], w["n_dev"], layout, schedule=sra.SCHEDULE_FUSED,
+                                   order=sra.ORDER_ORIGINAL)
+        dq, dk, dv = sra.ring_attn_bwd(x["q"], x["k"], x["v"], o, lse, x["do"], w["n_dev"], layout,
+                                       order=sra.ORDER_ORIGINAL)
+        torch.cuda.synchronize()
+        errs = [float(np.abs(np64(g[:, :, heads]) - r).max()) for g, r in zip((dq, dk, dv), ref)]
+        say(f"bwd short original order layout={layout}: dq {errs[0]:.3g} dk {errs[1]:.3g} dv {errs[2]:.3g}")
+        assert max(errs) <= 2e-2, errs
+
+
 def test_bwd_short_sum_rules_and_first_row(sra, short_bwd):
     """Rows of P sum to 1, so sum_k dV_k = sum_i dO_i; shifting every key by the
     same vector leaves O unchanged, so sum_k dK_k = 0; row 0 sees only itself,

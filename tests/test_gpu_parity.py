@@ -290,6 +290,24 @@ def test_fwd_short_bf16_fused_dense_parity(sra, short_case, layout):
     assert (lse - l2).abs().max().item() <= 1e-4
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fwd_short_original_order_fused_dense_parity(sra, short_case, layout):
+    """The launch the benchmark times: Short, fused schedule, tensors in original
+    token order (each device's stripe read in place). Every row and head against
+    the dense fp64 oracle, and bit-identical to the device-layout path."""
+    w = WORKLOADS["short"]
+    x, o_ref, l_ref = short_case
+    o, lse = sra.ring_attn_fwd(x["q"], x["k"], x["v"], w["n_dev"], layout, schedule=sra.SCHEDULE_FUSED,
+                               order=sra.ORDER_ORIGINAL)
+    torch.cuda.synchronize()
+    e_o, e_l = maxabs(np64(o), o_ref), maxabs(np64(lse), l_ref)
+    say(f"short fused original order layout={layout}: O max-abs {e_o:.3g}  LSE {e_l:.3g}")
+    assert e_o <= 2e-2 and e_l <= 2e-2
+    assert torch.equal(o[:, 0], x["v"][:, 0])
+    o_d, l_d, _ = run_full_fused(sra, x, w["n_dev"], layout)
+    assert torch.equal(o, o_d) and torch.equal(lse, l_d)
+
+
 @pytest.mark.parametrize("S,N,H", [(8 * 200, 8, 2), (1024, 1, 2), (16, 16, 1), (4 * 300, 4, 3),
                                    (64, 1, 1), (128, 1, 2), (192, 1, 1), (2 * 96, 2, 1)])
 def test_fwd_fused_small_dense_parity(sra, S, N, H):
