@@ -51,10 +51,10 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # on the stripe-permute copy kernel of known size; filled in from the counter
 # summary under profiles/ and valid only for the kernel sources it was taken on.
 TRAFFIC = {"workload": "short", "order": "original",
-           "kernel_sources_sha256": "c34b973a87006c107d0fc58b5cb73665df69407753a665da5a04351d2c54e1e2",
-           "bytes_per_launch": 603382955,
-           "fetch_bytes_per_launch": 565628600, "write_bytes_per_launch": 37754355,
-           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99945}}
+           "kernel_sources_sha256": "f95229d20802c114f368a5e05e8e87810abf3fc7a41af8ec2a5ccfeb71257915",
+           "bytes_per_launch": 162022412,
+           "fetch_bytes_per_launch": 124280945, "write_bytes_per_launch": 37741466,
+           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99988}}
 
 
 def parse():

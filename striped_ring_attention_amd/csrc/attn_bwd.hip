@@ -124,7 +124,11 @@ __global__ void __launch_bounds__(DQ_NT, 1) bwd_dq(BwdArgs a) {
     const int64_t span_bytes = (int64_t)(L - 1) * rstride + D * 2;
 
     // Rounds: in round r device d holds the block of device (d - r) mod N.
-    auto source = [&](int r) { return (d - r + a.N) % a.N; };
+    // Walk step u visits source device u (round (d - u) mod N): every device
+    // of a head walks the sources in the same order, so the workgroups of a
+    // head read the same K/V slab at the same time and share it through L2.
+    // The sum over rounds is the same in any order up to rounding.
+    auto source = [&](int u) { return u; };
     auto delta_of = [&](int r) { return clamp_delta(live_delta(a.layout, a.N, L, d, source(r)), L); };
     auto tiles_of = [&](int r) { return (live32(j1 - 1, delta_of(r), L) + QBN - 1) / QBN; };
     int n_tiles = 0;

@@ -82,10 +82,11 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     // Rounds: in round r the block of device s meets the queries of device
     // (s + r) mod N. Query rows that see any key of this workgroup start at
     // k0 - delta + 1 (the live keys of row j are those < j + delta).
-    auto qdev = [&](int r) {
-        const int x = s + r;
-        return x >= N ? x - N : x;
-    };
+    // Walk step u visits the queries of device u (round (u - s) mod N): the
+    // key blocks of every device of a head walk the query devices in the same
+    // order, so they read the same Q/dO slab at the same time and share it
+    // through L2. The sum over rounds is the same in any order up to rounding.
+    auto qdev = [&](int u) { return u; };
     auto delta_of = [&](int r) { return clamp_delta(live_delta(a.layout, N, L, qdev(r), s), L); };
     auto first_tile = [&](int r) { return min(max(k0 - delta_of(r) + 1, 0), L) / KBQ; };
     int n_tiles = 0;

@@ -101,26 +101,37 @@ struct __align__(16) SmemBf16 {
 constexpr int kWaitVm4 = 0x0F74;   // vmcnt(4)
 constexpr int kWaitVm8 = 0x0F78;   // vmcnt(8)
 
-// Walks the (round, key tile) pairs one workgroup visits, in ring order:
-// rounds r_lo .. r_hi-1, and within a round the key tiles of the source
-// device that hold at least one live key for the workgroup's last query row.
-// All fields are wave-uniform.
+// Walks the (round, key tile) pairs one workgroup visits: the rounds
+// r_lo .. r_hi-1 (see RoundGeom for their order), and within a round the key
+// tiles of the source device that hold at least one live key for the
+// workgroup's last query row. All fields are wave-uniform.
 struct TileCursor {
-    int r, kt, nt;        // round, key tile within the round, tiles in the round
+    int r, kt, nt;        // walk step, key tile within its round, tiles in the round
     int s, delta;         // source device of the round, live-key shift
 };
 
 struct RoundGeom {
     int L, N, layout, d, j_last, r_hi;
-    // Enter round c.r. 32-bit scalar arithmetic only: s = (d - r) mod N
-    // without a division (0 <= d, r < N). The shift is only ever used through
-    // live32(j, delta, L) with 0 <= j < L, so with a contiguous layout it is
-    // reduced to what that sees: a source after d has no live key for any
-    // query (-L-1), one before d has all of them (L+1), and s = d is the
-    // causal block (1).
+    int slab_walk;   // 1: step c.r of the walk visits source device s = c.r
+    // Enter step c.r of the walk. In ring order (one launch per round) step
+    // r is round r, whose source is s = (d - r) mod N, found with 32-bit
+    // scalar arithmetic and no division (0 <= d, r < N). The all-rounds
+    // launch visits the sources in the same order on every device instead
+    // (step u: source u, i.e. round (d - u) mod N): at any moment the
+    // workgroups of all devices of a head then read the same K/V slab, which
+    // they share through L2, while in ring order they would read N different
+    // slabs. The rounds' partial results combine the same way in any order
+    // (the log-sum-exp merge is exact), so only rounding differs.
+    // The shift is only ever used through live32(j, delta, L) with
+    // 0 <= j < L, so with a contiguous layout it is reduced to what that
+    // sees: a source after d has no live key for any query (-L-1), one before
+    // d has all of them (L+1), and s = d is the causal block (1).
     __device__ __forceinline__ void enter(TileCursor& c) const {
-        int s = d - c.r;
-        if (s < 0) s += N;
+        int s = c.r;
+        if (!slab_walk) {
+            s = d - c.r;
+            if (s < 0) s += N;
+        }
         const int dl = layout == 1 ? (s <= d ? 1 : 0) : (s == d ? 1 : (s < d ? L + 1 : -L - 1));
         c.s = __builtin_amdgcn_readfirstlane(s);
         c.delta = __builtin_amdgcn_readfirstlane(dl);
@@ -142,7 +153,8 @@ struct RoundGeom {
 
 // kFused = false: one ring round per launch (a.round), with the epilogue
 //   writing, merging or finishing per a.mode.
-// kFused = true: all N rounds in one launch; the online softmax carries the
+// kFused = true: all N rounds in one launch, visiting the source devices in
+//   the same order on every device (RoundGeom); the online softmax carries the
 //   running (O, max, sum) across rounds, which is the log-sum-exp merge of
 //   the per-round partial results, and the epilogue writes the output.
 //
@@ -169,7 +181,7 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     const int j0 = (int)blk.qt * BM;
     const int j1 = min(j0 + BM, L);
     const int d = (int)blk.d;
-    const RoundGeom geo{L, a.N, a.layout, d, j1 - 1, kFused ? a.N : a.round + 1};
+    const RoundGeom geo{L, a.N, a.layout, d, j1 - 1, kFused ? a.N : a.round + 1, kFused ? 1 : 0};
 
     // Tiles per round; device-side live-tile census.
     int n_tiles = 0;
@@ -179,7 +191,8 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
             geo.enter(c);
             n_tiles += c.nt;
             if (a.live_counts != nullptr && tid == 0 && c.nt > 0)
-                atomicAdd((unsigned long long*)&a.live_counts[(int64_t)c.r * a.N + d], (unsigned long long)c.nt);
+                atomicAdd((unsigned long long*)&a.live_counts[(int64_t)(c.s <= d ? d - c.s : d - c.s + a.N) * a.N + d],
+                          (unsigned long long)c.nt);
         }
     }
     if (!kFused && n_tiles == 0 && (flags & kFlagMerge) && !(flags & kFlagFinal)) return;   // merging nothing
