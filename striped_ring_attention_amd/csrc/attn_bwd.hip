@@ -18,7 +18,8 @@
 //
 //  * bwd_delta:  Delta = rowsum(dO * O) in fp32.
 //  * bwd_dq:     a workgroup owns 256 query rows (8 waves x 32) and walks
-//                the (round, 64-key tile) pairs in ring order. Per 32-key
+//                the (round, 64-key tile) pairs, taking the rounds in the
+//                same source order on every device. Per 32-key
 //                block: S^T = K Q^T and dP^T = V dO^T on MFMA (Q^T and dO^T
 //                held in registers, K and V row-major in LDS), then
 //                dS^T = P^T (dP^T - Delta) scale, and dQ^T += K^T dS^T with
@@ -26,7 +27,8 @@
 //                (ds_read_b64_tr_b16).
 //  * bwd_dkdv:   a workgroup owns 128 keys (4 groups x 32) of one source
 //                device and walks the 32-row query tiles of every device that
-//                meets the block, round by round. Two waves per 32-key group:
+//                meets the block, round by round (query devices in the same
+//                order for every key block). Two waves per 32-key group:
 //                one computes S = Q K^T, P and dV^T += dO^T P (K held in
 //                registers), the other dP = dO V^T, dS and dK^T += Q^T dS (V
 //                held in registers), P passing between them through LDS; Q and
@@ -94,7 +96,8 @@ struct __align__(16) SmemDq {
 };
 
 // A workgroup owns 256 query rows (8 waves x 32) of one device and walks the
-// (round, 64-key tile) pairs in ring order. Per 32-key block: S^T = K Q^T
+// (round, 64-key tile) pairs, the rounds in source-device order (see
+// source() below). Per 32-key block: S^T = K Q^T
 // and dP^T = V dO^T on MFMA (Q^T and dO^T held in registers, K and V rows
 // from LDS), dS^T = P^T (dP^T - Delta) scale with P^T = 2^(S^T scale log2 e -
 // LSE log2 e), then dQ^T += K^T dS^T with K^T read transposed from the
@@ -200,7 +203,7 @@ __global__ void __launch_bounds__(DQ_NT, 1) bwd_dq(BwdArgs a) {
     };
     auto row_off = [&](int kk) { return c32 * D + 8 * ((2 * kk + h2) ^ swz(c32)); };
 
-    // Tile cursor (round, key tile), in ring order.
+    // Tile cursor (walk step, key tile); walk step u visits source u.
     int cr = 0, ck = 0, cnt = tiles_of(0);
     auto settle = [&](int& r, int& k, int& nt) {
         while (k >= nt && r + 1 < a.N) {
