@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps before them (default per workload: past the clock ramp)")
     ap.add_argument("--workload", default="short")
+    ap.add_argument("--seq", type=int, default=None,
+                    help="override the workload's sequence length (the JSON then names the workload '<name>+override')")
+    ap.add_argument("--heads", type=int, default=None, help="override the workload's head count")
     ap.add_argument("--layout", default="striped", choices=["striped", "contiguous"])
     ap.add_argument("--schedule", default="fused", choices=["fused", "per_round"],
                     help="ring schedule of the timed step (the other one is timed alongside)")
@@ -244,8 +247,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     sra.load()
-    w = WORKLOADS[args.workload]
-    k_def, w_def = DEFAULT_STEPS.get(args.workload, (20, 3))
+    w = dict(WORKLOADS[args.workload])
+    over = {n: val for n, val in (("seq", args.seq), ("heads", args.heads)) if val is not None}
+    w.update(over)
+    wname = args.workload + ("+override" if over else "")
+    if over:
+        # Steps sized from the useful work at ~1 PFLOP/s: ~0.1 s of warm-up, ~0.3 s timed.
+        t_est = 2.0 * w["head_dim"] * w["batch"] * w["heads"] * w["seq"] ** 2 / 1e15
+        k_def, w_def = max(2, round(0.3 / t_est)), max(1, round(0.1 / t_est))
+    else:
+        k_def, w_def = DEFAULT_STEPS.get(args.workload, (20, 3))
     args.steps = k_def if args.steps is None else args.steps
     args.warmup = w_def if args.warmup is None else args.warmup
     if w["dtype"] != torch.bfloat16:
@@ -255,7 +266,10 @@ def main():
     layout = sra.STRIPED if args.layout == "striped" else sra.CONTIGUOUS
     sched = sra.SCHEDULE_FUSED if args.schedule == "fused" else sra.SCHEDULE_PER_ROUND
     dev = torch.device("cuda:0")
-    x = make_inputs(args.workload, device=dev, with_grad=not args.no_backward)
+    if w["seq"] % w["n_dev"] != 0:
+        print(f"--seq must be a multiple of the workload's {w['n_dev']} ring devices", file=sys.stderr)
+        sys.exit(2)
+    x = make_inputs(w, device=dev, with_grad=not args.no_backward)
     q, k, v = x["q"], x["k"], x["v"]
     qd, kd, vd = (torch.empty_like(t) for t in (q, k, v))
     o_dev = torch.empty_like(q)
@@ -476,17 +490,17 @@ def main():
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "seq_len": S, "heads": H, "head_dim": D,
+        "config": {"workload": wname, "batch": B, "seq_len": S, "heads": H, "head_dim": D,
                    "ring_devices": N, "layout": args.layout, "schedule": args.schedule, "order": args.order,
                    "causal": True,
                    "pass": "forward"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": stored_traffic(args.workload, sched, layout, args.order),
+                     "traffic": stored_traffic(wname, sched, layout, args.order),
                      "kernel": "round_fwd_bf16_d128<fused>" if sched == sra.SCHEDULE_FUSED
                      else "round_fwd_bf16_d128<per-round>",
-                     "traffic_detail": traffic_detail(args.workload, sched, layout, args.order),
+                     "traffic_detail": traffic_detail(wname, sched, layout, args.order),
                      "launches_per_step": nl, "avg_launch_ms": attn_ms / nl,
                      "step_kernel_ms_median_min_max": [statistics.median(ring_ms_steps), min(ring_ms_steps),
                                                        max(ring_ms_steps)],
