@@ -51,10 +51,10 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # on the stripe-permute copy kernel of known size; filled in from the counter
 # summary under profiles/ and valid only for the kernel sources it was taken on.
 TRAFFIC = {"workload": "short", "order": "original",
-           "kernel_sources_sha256": "f95229d20802c114f368a5e05e8e87810abf3fc7a41af8ec2a5ccfeb71257915",
-           "bytes_per_launch": 162022412,
-           "fetch_bytes_per_launch": 124280945, "write_bytes_per_launch": 37741466,
-           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99988}}
+           "kernel_sources_sha256": "270e88977a1870ebf812f97bfa4f2c0789acebc6c1239fb999ab4d6af5a06b9e",
+           "bytes_per_launch": 161893422,
+           "fetch_bytes_per_launch": 124151245, "write_bytes_per_launch": 37742177,
+           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99992}}
 
 
 def parse():

@@ -201,9 +201,12 @@ size_t sra_fwd_workspace_bytes(const sra_desc* desc);
  * sra_fwd_workspace_bytes(desc) bytes (contents undefined on entry/exit).
  * live_counts: NULL or device int64 [N*N]; tiles are ADDED as above.
  * round_events: NULL, or a host array of hipEvent_t (passed as void*): with
- * SRA_SCHEDULE_PER_ROUND 2*N events, recorded on `stream` before and after
- * each round's launch; with SRA_SCHEDULE_FUSED 2 events around the launch.
- * The events must have been created by the caller. */
+ * SRA_SCHEDULE_PER_ROUND 2*N events bracketing each round's kernel, with
+ * SRA_SCHEDULE_FUSED 2 events bracketing the one launch. For bf16 the
+ * dispatch itself records them at the kernel's start and end; for fp32 they
+ * are recorded on `stream` before and after the launch. A launch with no
+ * work still records both. The events must have been created by the caller,
+ * with timing enabled. */
 int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k,
                       const void* v, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, int64_t* live_counts,

@@ -37,6 +37,8 @@
 //    tiles ahead of the step that first reads them;
 //    16-byte chunks are XOR-swizzled per row so both MFMA operand read
 //    patterns are bank-conflict-free.
+#include <hip/hip_ext.h>
+
 #include "kernel_common.h"
 
 namespace sra {
@@ -587,14 +589,29 @@ int flags_of(const RoundArgs& a) {
 
 }  // namespace
 
-hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t stream) {
+hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t stream, hipEvent_t start,
+                                  hipEvent_t stop) {
     const int64_t nqt = (a.L + BM - 1) / BM;
     const int64_t blocks = nqt * a.H * (a.dev_hi - a.dev_lo) * a.B;
-    if (blocks == 0) return hipSuccess;
-    if (fused)
-        hipLaunchKernelGGL(round_fwd_bf16_d128<true>, dim3((unsigned)blocks), dim3(NT), 0, stream, a, 0);
-    else
-        hipLaunchKernelGGL(round_fwd_bf16_d128<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, a, flags_of(a));
+    if (blocks == 0) {
+        // Nothing to launch: the events still mark this point of the stream.
+        if (start != nullptr && hipEventRecord(start, stream) != hipSuccess) return hipGetLastError();
+        if (stop != nullptr && hipEventRecord(stop, stream) != hipSuccess) return hipGetLastError();
+        return hipSuccess;
+    }
+    // With events, the dispatch itself records them at the kernel's start and
+    // end (no separate marker packets around the launch).
+    const dim3 grid((unsigned)blocks), block(NT);
+    if (start != nullptr || stop != nullptr) {
+        if (fused)
+            hipExtLaunchKernelGGL(round_fwd_bf16_d128<true>, grid, block, 0, stream, start, stop, 0, a, 0);
+        else
+            hipExtLaunchKernelGGL(round_fwd_bf16_d128<false>, grid, block, 0, stream, start, stop, 0, a, flags_of(a));
+    } else if (fused) {
+        hipLaunchKernelGGL(round_fwd_bf16_d128<true>, grid, block, 0, stream, a, 0);
+    } else {
+        hipLaunchKernelGGL(round_fwd_bf16_d128<false>, grid, block, 0, stream, a, flags_of(a));
+    }
     return hipGetLastError();
 }
 

@@ -104,9 +104,19 @@ sra::RoundArgs make_args(const sra_desc* d, const void* q, const void* k, const 
     return a;
 }
 
-hipError_t launch_round(const sra_desc* d, const sra::RoundArgs& a, hipStream_t s, bool fused = false) {
-    if (d->dtype == SRA_DTYPE_BF16) return sra::launch_round_bf16_d128(a, fused, s);
-    return sra::launch_round_f32(a, d->head_dim, s);
+// Launch one round (or, fused, all of them). With events: the bf16 kernels
+// have the dispatch record them at the kernel's start and end; the fp32
+// kernels are bracketed by event records on the stream.
+hipError_t launch_round(const sra_desc* d, const sra::RoundArgs& a, hipStream_t s, bool fused = false,
+                        hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
+    if (d->dtype == SRA_DTYPE_BF16) return sra::launch_round_bf16_d128(a, fused, s, start, stop);
+    if (start != nullptr) {
+        const hipError_t e = hipEventRecord(start, s);
+        if (e != hipSuccess) return e;
+    }
+    const hipError_t e = sra::launch_round_f32(a, d->head_dim, s);
+    if (e != hipSuccess || stop == nullptr) return e;
+    return hipEventRecord(stop, s);
 }
 
 int64_t elem_bytes(const sra_desc* d) { return d->dtype == SRA_DTYPE_BF16 ? 2 : 4; }
@@ -302,32 +312,18 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k, const 
     if (desc->schedule == SRA_SCHEDULE_FUSED) {
         a.round = 0;
         a.mode = 3;
-        if (round_events) {
-            hipError_t e = hipEventRecord((hipEvent_t)round_events[0], s);
-            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
-        }
-        hipError_t e = launch_round(desc, a, s, true);
+        hipError_t e = launch_round(desc, a, s, true, round_events ? (hipEvent_t)round_events[0] : nullptr,
+                                    round_events ? (hipEvent_t)round_events[1] : nullptr);
         if (e != hipSuccess) return hip_status(e, "fused ring launch");
-        if (round_events) {
-            e = hipEventRecord((hipEvent_t)round_events[1], s);
-            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
-        }
         return SRA_OK;
     }
     for (int r = 0; r < N; ++r) {
         a.round = r;
         if (bf16) a.mode = r == 0 ? (N == 1 ? 3 : 0) : (r == N - 1 ? 2 : 1);
         else a.mode = r == 0 ? 0 : 1;   // fp32: the accumulator is the output
-        if (round_events) {
-            hipError_t e = hipEventRecord((hipEvent_t)round_events[2 * r], s);
-            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
-        }
-        hipError_t e = launch_round(desc, a, s);
+        hipError_t e = launch_round(desc, a, s, false, round_events ? (hipEvent_t)round_events[2 * r] : nullptr,
+                                    round_events ? (hipEvent_t)round_events[2 * r + 1] : nullptr);
         if (e != hipSuccess) return hip_status(e, "ring round launch");
-        if (round_events) {
-            e = hipEventRecord((hipEvent_t)round_events[2 * r + 1], s);
-            if (e != hipSuccess) return hip_status(e, "hipEventRecord");
-        }
     }
     return SRA_OK;
 }

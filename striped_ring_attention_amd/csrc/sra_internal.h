@@ -61,7 +61,9 @@ struct RoundArgs {
                          // 3: write the partial as the output (o_final, lse_acc)
 };
 
-hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t stream);
+// start / stop: optional events recorded by the dispatch at the kernel's start and end.
+hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t stream, hipEvent_t start = nullptr,
+                                  hipEvent_t stop = nullptr);
 
 // Backward of the whole ring (every round), bf16 with head dim 128.
 struct BwdArgs {
