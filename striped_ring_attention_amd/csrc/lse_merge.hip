@@ -30,7 +30,9 @@ __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, flo
 
 // One thread per 4 consecutive values of a row; the Dh/4 threads of one row
 // sit in one wavefront (Dh <= 256), so every lane reads lse_acc[row] before
-// the row's first lane overwrites it.
+// the row's first lane overwrites it. O values are touched once, so they are
+// streamed with non-temporal loads and stores, which keeps them from
+// displacing cached data.
 __global__ void __launch_bounds__(256) lse_merge_kernel(f32x4* __restrict__ o_acc, float* __restrict__ lse_acc,
                                                         const f32x4* __restrict__ o_part,
                                                         const float* __restrict__ lse_part, uint64_t rows,
@@ -43,7 +45,7 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(f32x4* __restrict__ o_ac
         float la = lse_acc[row], lb = lse_part[row];
         float wa, wb, l;
         merge_weights(la, lb, wa, wb, l);
-        f32x4 a = o_acc[c], b = o_part[c];
+        f32x4 a = __builtin_nontemporal_load(&o_acc[c]), b = __builtin_nontemporal_load(&o_part[c]);
         f32x4 r;
         if (l == -INFINITY) {
             r = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -53,7 +55,7 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(f32x4* __restrict__ o_ac
             if (wb != 0.f) r = (wa != 0.f) ? r + wb * b : wb * b;
             if (wa == 0.f) r = wb * b;
         }
-        o_acc[c] = r;
+        __builtin_nontemporal_store(r, &o_acc[c]);
         if (part == 0) lse_acc[row] = l;
     }
 }
