@@ -70,8 +70,10 @@ __global__ void __launch_bounds__(kRopeThreads) rope_gather(RopeArgs a) {
     const int work = (int)a.H * groups;
     for (int i = threadIdx.x; i < work; i += kRopeThreads) {
         const int h = i / groups, c0 = 4 * (i - h * groups);
-        const V4 lo = *(const V4*)(xr + h * a.D + c0);
-        const V4 hi = *(const V4*)(xr + h * a.D + half + c0);
+        // Each value is read and written once: non-temporal accesses keep the
+        // stream from displacing cached data.
+        const V4 lo = __builtin_nontemporal_load((const V4*)(xr + h * a.D + c0));
+        const V4 hi = __builtin_nontemporal_load((const V4*)(xr + h * a.D + half + c0));
         V4 ylo, yhi;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -80,8 +82,8 @@ __global__ void __launch_bounds__(kRopeThreads) rope_gather(RopeArgs a) {
             ylo[e] = (T)__builtin_fmaf(xl, w.x, -xh * w.y);
             yhi[e] = (T)__builtin_fmaf(xl, w.y, xh * w.x);
         }
-        *(V4*)(yr + h * a.D + c0) = ylo;
-        *(V4*)(yr + h * a.D + half + c0) = yhi;
+        __builtin_nontemporal_store(ylo, (V4*)(yr + h * a.D + c0));
+        __builtin_nontemporal_store(yhi, (V4*)(yr + h * a.D + half + c0));
     }
 }
 
