@@ -22,11 +22,18 @@ roofline = the ring attention kernel (the dominant kernel): useful flops of
          the bf16 dense MFMA peak.
 Timing: the default warm-up and step counts depend on the workload (Short:
 300 untimed, then 300 timed steps) so that the timed region runs at the
-GPU's sustained clocks; each secondary section is preceded by ~0.15 s of the
-same work, and short kernels are timed behind queued GPU work.
-cpu_baseline = the CPU oracle (fp64 numpy dense causal attention) on a
-         bounded sample of the same workload (whole sequence, heads cycled
-         until about --cpu-seconds of work), rank 0 only.
+GPU's sustained clocks; each secondary section is preceded by at least
+~0.15 s of the same work, and short kernels are timed behind queued GPU work.
+cpu_baseline = the CPU oracle (fp64 numpy causal attention, oracle.attention_rows)
+         on a bounded sample of the same workload: 64-row blocks of one head
+         at fixed, evenly spaced positions, visited in a fixed order until
+         about --cpu-seconds of work; its useful TFLOP/s is extrapolated to the
+         whole forward by useful-pair count.
+The default workload is the longest one (786,432 tokens, 32 heads, 16 ring
+devices, forward plus backward): --steps and --warmup count its forward
+launches; the backward is timed in the same run over a few calls and
+reported with its own roofline fraction, and the secondary sections (other
+schedule, contiguous layout, device order, simulated ring) use few steps.
 """
 
 import argparse
@@ -45,16 +52,18 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
 FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
-# HBM traffic of one fused forward launch on the Short workload (striped,
-# tensors in the order named),
-# from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by the same counters
-# on the stripe-permute copy kernel of known size; filled in from the counter
-# summary under profiles/ and valid only for the kernel sources it was taken on.
-TRAFFIC = {"workload": "short", "order": "original",
-           "kernel_sources_sha256": "270e88977a1870ebf812f97bfa4f2c0789acebc6c1239fb999ab4d6af5a06b9e",
-           "bytes_per_launch": 161893422,
-           "fetch_bytes_per_launch": 124151245, "write_bytes_per_launch": 37742177,
-           "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99992}}
+# HBM traffic of one fused forward launch (striped, tensors in the order
+# named) per workload, from rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled
+# by the same counters on the stripe-permute copy kernel of known size;
+# filled in from the counter summaries under profiles/ and valid only for the
+# kernel sources they were taken on.
+TRAFFIC = [
+    {"workload": "short", "order": "original",
+     "kernel_sources_sha256": "270e88977a1870ebf812f97bfa4f2c0789acebc6c1239fb999ab4d6af5a06b9e",
+     "bytes_per_launch": 161893422,
+     "fetch_bytes_per_launch": 124151245, "write_bytes_per_launch": 37742177,
+     "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99992}},
+]
 
 
 def parse():
@@ -64,7 +73,8 @@ def parse():
                     help="timed steps (default per workload: about 0.1-1 s of timed GPU work)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps before them (default per workload: past the clock ramp)")
-    ap.add_argument("--workload", default="short")
+    ap.add_argument("--workload", default="very_long",
+                    help="tiny/short/mid/long/very_long (default: very_long, the longest single-GPU shape)")
     ap.add_argument("--seq", type=int, default=None,
                     help="override the workload's sequence length (the JSON then names the workload '<name>+override')")
     ap.add_argument("--heads", type=int, default=None, help="override the workload's head count")
@@ -76,7 +86,10 @@ def parse():
                          "kernel's row addressing (one launch per step); device: gather into the striped "
                          "device layout, ring, gather back (the other one is timed alongside)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--sec-steps", type=int, default=None,
+                    help="timed steps of each secondary section (default per workload)")
+    ap.add_argument("--bwd-steps", type=int, default=None, help="timed backward calls (default per workload)")
     ap.add_argument("--no-compare", action="store_true", help="skip the other-schedule and contiguous runs")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-critical-path", action="store_true",
@@ -89,19 +102,31 @@ def parse():
 # (a Short forward launch takes 330-380 us over its first 40 launches, then a
 # steady ~300 us for as long as it runs), so the warm-up spans >= 100 ms and
 # the timed region measures the sustained rate.
-DEFAULT_STEPS = {"short": (300, 300), "mid": (10, 4), "long": (3, 1), "very_long": (2, 1)}
+DEFAULT_STEPS = {"short": (300, 300), "mid": (10, 4), "long": (3, 1), "very_long": (5, 1)}
+# Timed steps of each secondary section (other schedule, layout or order; the
+# simulated ring's repetitions) and timed backward calls, at most. A Very long
+# forward takes ~4.4 s and its backward ~16 s, so these stay small there.
+SECONDARY_CAP = {"short": 300, "mid": 10, "long": 3, "very_long": 2}
+BACKWARD_CAP = {"short": 100, "mid": 10, "long": 3, "very_long": 2}
+RING_SIM_REPS = {"long": 1, "very_long": 1}
 WARM_SECONDS = 0.15   # back-to-back work before each secondary timed section
 
 
+def note(msg):
+    """Progress line on stderr (stdout carries only the JSON result)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def warm(torch, fn, seconds=WARM_SECONDS):
-    """Run `fn` back to back for about `seconds`, so the section that follows
-    starts at sustained clocks instead of after host-side idle time."""
+    """Run `fn` back to back for at least `seconds` (at least once), so the
+    section that follows starts at sustained clocks instead of after host-side
+    idle time."""
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     fn()
     torch.cuda.synchronize()
-    n = max(1, int(seconds / max(time.perf_counter() - t0, 1e-5)))
-    for _ in range(n):
+    dt = max(time.perf_counter() - t0, 1e-5)
+    for _ in range(max(0, int(seconds / dt) - 1)):
         fn()
     torch.cuda.synchronize()
 
@@ -132,30 +157,66 @@ def imbalance(live):
     return per, agg
 
 
-def cpu_baseline(x, seconds):
-    """Time the oracle on whole-sequence heads until ~`seconds` have elapsed."""
-    import oracle
+def blas_info():
+    """numpy's BLAS library and thread count (threadpoolctl), or None."""
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "library": os.path.basename(i.get("filepath", ""))}
     except Exception:  # pragma: no cover
-        blas_threads = None
-    q, k, v = (x[n].cpu() for n in ("q", "k", "v"))
-    B, S, H, D = q.shape
-    done, t_total = 0, 0.0
-    while t_total < seconds and done < 4 * H:
-        h = done % H
-        qh, kh, vh = (t[:, :, h:h + 1].double().numpy() for t in (q, k, v))
-        t0 = time.perf_counter()
-        oracle.dense_causal_attention(qh, kh, vh)
-        t_total += time.perf_counter() - t0
-        done += 1
-    flops = 4.0 * D * B * done * S * (S + 1) / 2
+        return None
+    return None
+
+
+def cpu_baseline(x, seconds, block=64, n_blocks=64):
+    """The oracle's useful rate on a bounded sample of the workload, extrapolated.
+
+    Sample: head 0 of batch 0; `n_blocks` blocks of `block` consecutive query
+    rows at evenly spaced positions over the sequence, visited in a fixed
+    (seeded) order until about `seconds` of oracle time. Each block is one
+    call of oracle.attention_rows (fp64 numpy: the block's scores against
+    every key up to its last row, masked, softmax, times V). Useful flops are
+    4*Dh per live causal pair of the sampled rows; the whole forward's time is
+    extrapolated from that rate and the workload's pair count."""
+    import numpy as np
+    import oracle
     cores = len(os.sched_getaffinity(0))
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads or cores,
-            "kind": "oracle", "sample": f"{done} head passes (heads cycled, {H} heads in the workload), whole "
-                                        f"sequence S={S}, fp64 numpy dense causal attention, {t_total:.1f} s; "
-                                        f"host has {cores} cores available"}
+    B, S, H, D = x["q"].shape
+    qh, kh, vh = (x[n][:1, :, :1].cpu() for n in ("q", "k", "v"))
+    blas = blas_info()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:  # pragma: no cover
+        limiter = None
+    blas_used = blas_info()
+    nb = min(n_blocks, max(1, S // block))
+    starts = [min(S - block, (m * S) // nb) if S >= block else 0 for m in range(nb)]
+    order = np.random.default_rng(0).permutation(nb)
+    done, pairs, t_total = 0, 0, 0.0
+    for m in order:
+        if t_total >= seconds:
+            break
+        i0 = starts[m]
+        rows = np.arange(i0, min(S, i0 + block))
+        t0 = time.perf_counter()
+        oracle.attention_rows(qh, kh, vh, rows)
+        t_total += time.perf_counter() - t0
+        pairs += int((rows + 1).sum())
+        done += 1
+    if limiter is not None:
+        limiter.restore_original_limits()
+    rate = 4.0 * D * pairs / t_total / 1e12
+    full_flops = 4.0 * D * B * H * S * (S + 1) / 2
+    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} blocks of {block} consecutive query rows (head 0 of {H}, batch 0) at fixed, "
+                      f"evenly spaced positions of the {S}-token sequence, {pairs} useful causal pairs, fp64 numpy "
+                      f"oracle.attention_rows, {t_total:.1f} s; rate extrapolated to the whole forward by "
+                      f"useful-pair count",
+            "extrapolated": True, "extrapolated_full_forward_s": full_flops / (rate * 1e12),
+            "blas": blas_used or blas, "cores_note": "len(os.sched_getaffinity(0)); BLAS threads limited to it"}
 
 
 def queried_peak_bf16(torch):
@@ -184,28 +245,38 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def stored_traffic(workload, sched, layout, order):
-    """HBM bytes per launch of the fused forward kernel from the last counter
-    runs, or None when they do not cover this configuration or the kernel's
-    sources have changed since they were taken."""
-    t = TRAFFIC
-    if (t is None or workload != t["workload"] or sched != 1 or layout != 1 or order != t["order"]
-            or kernel_source_digest() != t["kernel_sources_sha256"]):
+def traffic_record(workload, sched, layout, order):
+    """The counter record of the fused forward kernel for this configuration,
+    or None when none covers it or the kernel's sources have changed since
+    the counters were taken."""
+    if sched != 1 or layout != 1:
         return None
-    return t["bytes_per_launch"]
+    digest = kernel_source_digest()
+    for t in TRAFFIC:
+        if t["workload"] == workload and t["order"] == order and t["kernel_sources_sha256"] == digest:
+            return t
+    return None
+
+
+def stored_traffic(workload, sched, layout, order):
+    """HBM bytes per launch of the fused forward kernel, or None (see traffic_record)."""
+    t = traffic_record(workload, sched, layout, order)
+    return None if t is None else t["bytes_per_launch"]
 
 
 def traffic_detail(workload, sched, layout, order):
-    if stored_traffic(workload, sched, layout, order) is None:
+    t = traffic_record(workload, sched, layout, order)
+    if t is None:
         return None
-    return {k: TRAFFIC[k] for k in ("fetch_bytes_per_launch", "write_bytes_per_launch", "copy_scale")}
+    return {k: t[k] for k in ("fetch_bytes_per_launch", "write_bytes_per_launch", "copy_scale")}
 
 
 def time_backward(sra, torch, x, N, layout, ordr, fwd_step, qd, kd, vd, o_dev, lse_dev, o, lse, K, useful_fwd_flops):
-    """The ring backward (dQ, dK, dV) on the forward's device-layout outputs:
-    K launches of the three backward kernels, each bracketed by events on the
-    current stream. Useful flops: 10*Dh per live causal pair (S recomputed,
-    dP, dV, dQ, dK), i.e. 2.5x the forward's."""
+    """The ring backward (dQ, dK, dV) on the forward's outputs, in the step's
+    order: after at least ~0.15 s of untimed calls, K calls of the three
+    backward kernels, each bracketed by events on the current stream (the
+    stream the kernels are launched on). Useful flops: 10*Dh per live causal
+    pair (S recomputed, dP, dV, dQ, dK), i.e. 2.5x the forward's."""
     fwd_step()
     if layout == sra.STRIPED and ordr == sra.ORDER_DEVICE:
         q, k, v, out, l = qd, kd, vd, o_dev, lse_dev
@@ -223,11 +294,17 @@ def time_backward(sra, torch, x, N, layout, ordr, fwd_step, qd, kd, vd, o_dev, l
         sra.ring_attn_bwd(q, k, v, out, l, do, N, layout, dq=dq, dk=dk, dv=dv, workspace=ws, order=ordr)
         b.record()
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    per_call = [a.elapsed_time(b) for a, b in evs]
+    ms = sum(per_call) / K
     flops = 2.5 * useful_fwd_flops
-    return {"ms": ms, "useful_TFLOPs": flops / (ms * 1e-3) / 1e12, "pct_bf16_peak": 100 * flops / (ms * 1e-3) / 1e12
-            / PEAK_BF16_TFLOPS, "flops_per_live_pair": "10*head_dim", "kernels": ["bwd_delta", "bwd_dq", "bwd_dkdv"],
-            "launches": K, "note": "not part of value: the headline metric is the forward"}
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "ms_per_call": per_call, "useful_TFLOPs": achieved,
+            "pct_bf16_peak": 100 * achieved / PEAK_BF16_TFLOPS,
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_BF16_TFLOPS, "flops_per_call": flops},
+            "flops_per_live_pair": "10*head_dim", "kernels": ["bwd_delta", "bwd_dq", "bwd_dkdv"],
+            "calls": K, "order": "original" if ordr == sra.ORDER_ORIGINAL else "device",
+            "note": "not part of value: the headline is the forward; one call = the three backward kernels"}
 
 
 def main():
@@ -336,11 +413,16 @@ def main():
         step(layout, sched)
     torch.cuda.synchronize()
 
+    note(f"{wname}: census pass and {args.warmup} warm-up steps done")
     K = args.steps
+    base = args.workload
+    sec_K = args.sec_steps if args.sec_steps is not None else min(K, SECONDARY_CAP.get(base, K))
+    bwd_K = args.bwd_steps if args.bwd_steps is not None else min(K, BACKWARD_CAP.get(base, K))
     wall0 = time.perf_counter()
     dev_striped = ordr == sra.ORDER_DEVICE and layout == sra.STRIPED
     ms_step, per_launch, perm_ev = timed(layout, sched, K, perm=dev_striped)
     wall = time.perf_counter() - wall0
+    note(f"{K} timed steps done ({wall:.1f} s)")
     attn_ms = sum(sum(p) for p in per_launch) / K
     ring_ms_steps = [sum(p) for p in per_launch]   # kernel time of each timed step
     nl = launches(sched)
@@ -359,13 +441,14 @@ def main():
     dev_step = None
     if layout == sra.STRIPED and not dev_striped:
         warm(torch, lambda: step(layout, sched, od=sra.ORDER_DEVICE))
-        d_step, d_launch, perm_ev = timed(layout, sched, K, perm=True, od=sra.ORDER_DEVICE)
-        d_attn = sum(sum(p) for p in d_launch) / K
+        d_step, d_launch, perm_ev = timed(layout, sched, sec_K, perm=True, od=sra.ORDER_DEVICE)
+        d_attn = sum(sum(p) for p in d_launch) / sec_K
         dev_step = {"step_ms": d_step, "step_useful_TFLOPs": useful_flops / (d_step * 1e-3) / 1e12,
                     "ring_ms": d_attn, "ring_useful_TFLOPs": useful_flops / (d_attn * 1e-3) / 1e12}
     if layout == sra.STRIPED:
-        p_ms = sum(perm_ev[i][0].elapsed_time(perm_ev[i][1]) for i in range(K)) / K
-        u_ms = sum(perm_ev[i][2].elapsed_time(perm_ev[i][3]) for i in range(K)) / K
+        n_ev = len(perm_ev)
+        p_ms = sum(perm_ev[i][0].elapsed_time(perm_ev[i][1]) for i in range(n_ev)) / n_ev
+        u_ms = sum(perm_ev[i][2].elapsed_time(perm_ev[i][3]) for i in range(n_ev)) / n_ev
         el = q.element_size()
         p_bytes = 3 * 2 * q.numel() * el
         u_bytes = 2 * (o.numel() * el + lse.numel() * 4)
@@ -373,6 +456,7 @@ def main():
                 "unstripe_o_lse_ms": u_ms, "unstripe_GBps": u_bytes / (u_ms * 1e-3) / 1e9,
                 "hbm_peak_GBps": PEAK_HBM_GBS, "note": "timed back to back inside the step (caches warm)"}
 
+    note("device-order step done")
     # Cold-cache rates: the 256 MB Infinity Cache is flushed (a 1 GiB write)
     # before each repetition; median of 5.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.device)
@@ -429,6 +513,7 @@ def main():
              "note": "standalone unfused merge of one fp32 partial, rows B*S*H; not part of value"}
     del flush, m_oa, m_op, m_la, m_lp
 
+    note("gathers, rotary gather and merge done")
     # Imbalance: host census at 128x128 tiles and at the kernel's own tiles; device counters.
     tq, tk = sra.kernel_tiles(torch.bfloat16, D)
     imb = {}
@@ -456,13 +541,15 @@ def main():
             if lay == layout and sc == sched:
                 continue
             warm(torch, lambda: step(lay, sc))
-            c_step, c_launch, _ = timed(lay, sc, K)
-            c_attn = sum(sum(p) for p in c_launch) / K
+            c_step, c_launch, _ = timed(lay, sc, sec_K)
+            c_attn = sum(sum(p) for p in c_launch) / sec_K
             rec = {"ring_ms": c_attn, "ring_useful_TFLOPs": useful_flops / (c_attn * 1e-3) / 1e12,
                    "step_ms": c_step}
             if sc == sra.SCHEDULE_PER_ROUND:
-                rec["round_ms"] = [sum(c_launch[i][r] for i in range(K)) / K for r in range(N)]
+                rec["round_ms"] = [sum(c_launch[i][r] for i in range(sec_K)) / sec_K for r in range(N)]
+            rec["steps"] = sec_K
             compare[cname] = rec
+            note(f"compare {cname} done")
         compare[f"{args.layout}_{args.schedule}"] = {"ring_ms": attn_ms, "ring_useful_TFLOPs": attn_tflops,
                                                      "step_ms": ms_step}
         if dev_step is not None:
@@ -472,19 +559,23 @@ def main():
     if not args.no_critical_path:
         from striped_ring_attention_amd import ring_sim
         warm(torch, lambda: step(sra.CONTIGUOUS, sra.SCHEDULE_PER_ROUND))
-        t_c = ring_sim.time_device_rounds(q, k, v, N, sra.CONTIGUOUS, reps=3)
+        reps = RING_SIM_REPS.get(base, 3)
+        t_c = ring_sim.time_device_rounds(q, k, v, N, sra.CONTIGUOUS, reps=reps)
         for src, dst in ((q, qd), (k, kd), (v, vd)):
             sra.stripe_permute(src, N, out=dst)
         warm(torch, lambda: step(sra.STRIPED, sra.SCHEDULE_PER_ROUND))
-        t_s = ring_sim.time_device_rounds(qd, kd, vd, N, sra.STRIPED, reps=3)
+        t_s = ring_sim.time_device_rounds(qd, kd, vd, N, sra.STRIPED, reps=reps)
         critical = ring_sim.project(t_s, t_c, ring_sim.kv_block_bytes(B, S, H, D, N, q.element_size()))
         critical["note"] = ("one launch per (device, round) on this GPU; ring time = sum over rounds of "
                             "max(slowest device, K/V transfer at the assumed link bandwidth)")
+        critical["reps"] = reps
+        note("simulated ring done")
 
     backward = None
     if not args.no_backward:
         backward = time_backward(sra, torch, x, N, layout, ordr, lambda: step(layout, sched), qd, kd, vd, o_dev,
-                                 lse_dev, o, lse, K, useful_flops)
+                                 lse_dev, o, lse, bwd_K, useful_flops)
+        note("backward done")
 
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -512,6 +603,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        note("cpu baseline done")
     print(json.dumps(rec), flush=True)
 
 

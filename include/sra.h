@@ -136,7 +136,11 @@ int sra_kernel_tiles(const sra_desc* desc, int32_t* tile_q, int32_t* tile_k);
 
 /* Gather into striped device layout: viewing x and y as [outer, seq, row]
  * with `row_bytes` bytes per row, y[o, d*L + j, :] = x[o, j*N + d, :].
- * Bit-exact copy; x and y must not overlap; row_bytes % 4 == 0. */
+ * Bit-exact copy; x and y must not overlap; row_bytes % 4 == 0 and
+ * row_bytes <= 2^31; x and y 4-byte aligned (16-byte aligned with row_bytes
+ * % 16 == 0 takes the 16-byte path). outer >= 1; seq and n_dev as in
+ * sra_stripe_index. Errors: SRA_ERR_INVALID_ARG before any work is
+ * enqueued; SRA_ERR_HIP if the launch fails. */
 int sra_stripe_permute(const void* x, void* y, int64_t outer, int64_t seq,
                        int64_t row_bytes, int32_t n_dev, void* stream);
 
@@ -186,7 +190,18 @@ int sra_ring_round_attn(const sra_desc* desc, int32_t round, int32_t device,
  *   M = max(lse_acc, lse_part); lse = M + log(exp(lse_acc-M) + exp(lse_part-M));
  *   o_acc = exp(lse_acc-lse) o_acc + exp(lse_part-lse) o_part.
  * A side with LSE = -inf contributes nothing; both -inf gives o = 0,
- * LSE = -inf. This is how per-round partial results combine exactly. */
+ * LSE = -inf. Passage: each device attends to one circulating K/V block per
+ * round ("Summary" ¶1) and the ring computes attention exactly, not an
+ * approximation of it (abstract, pith.science/paper/2311.09431; "Summary"
+ * ¶2); softmax partial results over disjoint key
+ * sets combine exactly by this rule, which is how the per-round results of
+ * one device become its attention over every key.
+ * o_acc, o_part: device fp32 [rows, head_dim], 16-byte aligned; lse_acc,
+ * lse_part: device fp32 [rows]. o_acc/lse_acc are read and overwritten;
+ * o_part/lse_part are read only and must not overlap them. head_dim a
+ * power of two in [4, 256]; rows >= 0 (0 is a no-op). Errors:
+ * SRA_ERR_INVALID_ARG for a null pointer, bad head_dim or misalignment (no
+ * work enqueued); SRA_ERR_HIP if the launch fails. */
 int sra_lse_merge(float* o_acc, float* lse_acc, const float* o_part,
                   const float* lse_part, int64_t rows, int64_t head_dim,
                   void* stream);
@@ -195,6 +210,15 @@ int sra_lse_merge(float* o_acc, float* lse_acc, const float* o_part,
 size_t sra_fwd_workspace_bytes(const sra_desc* desc);
 
 /* The whole ring forward: all N rounds for all N devices, merged.
+ * Passage: "Summary" ¶1 (each device keeps its queries while the K/V blocks
+ * travel around the ring, one block per round, until every device has met
+ * every block; tiles that are entirely masked are skipped) and ¶2 (with the
+ * striped layout every device does about half of each round's work, and the
+ * result is exact). With SRA_SCHEDULE_PER_ROUND round r is one launch whose
+ * epilogue merges into the running result (sra_lse_merge's rule); with
+ * SRA_SCHEDULE_FUSED one launch walks every round per query tile and
+ * carries the online softmax across rounds, visiting the source devices in
+ * the same order on every device (only the rounding order differs).
  * q, k, v: [B, S, H, Dh] in device layout (dtype of desc);
  * o: [B, S, H, Dh] in device layout, dtype of desc (bf16 rounded to nearest
  * even); lse: fp32 [B, S, H]. workspace: device memory of at least
@@ -206,7 +230,11 @@ size_t sra_fwd_workspace_bytes(const sra_desc* desc);
  * dispatch itself records them at the kernel's start and end; for fp32 they
  * are recorded on `stream` before and after the launch. A launch with no
  * work still records both. The events must have been created by the caller,
- * with timing enabled. */
+ * with timing enabled.
+ * o, lse and the workspace are written while q, k, v are still read: none
+ * of them may overlap q, k, v or one another (SRA_ERR_INVALID_ARG).
+ * Errors: SRA_ERR_INVALID_ARG / SRA_ERR_UNSUPPORTED / SRA_ERR_WORKSPACE
+ * before any work is enqueued; SRA_ERR_HIP if a launch fails. */
 int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k,
                       const void* v, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, int64_t* live_counts,
@@ -227,7 +255,9 @@ size_t sra_bwd_workspace_bytes(const sra_desc* desc);
  * meets the queries of device (s + r) mod N; dk and dv of a block sum over
  * rounds, dq of a device over the blocks it meets. Deterministic (no
  * atomics). workspace: at least sra_bwd_workspace_bytes(desc) bytes.
- * desc->schedule is ignored. Returns SRA_ERR_UNSUPPORTED for fp32. */
+ * desc->schedule is ignored. Returns SRA_ERR_UNSUPPORTED for fp32. dq, dk,
+ * dv and the workspace must not overlap any input or one another
+ * (SRA_ERR_INVALID_ARG). */
 int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k,
                       const void* v, const void* o, const float* lse,
                       const void* dout, void* dq, void* dk, void* dv,

@@ -595,9 +595,11 @@ hipError_t launch_round_bf16_d128(const RoundArgs& a, bool fused, hipStream_t st
     const int64_t blocks = nqt * a.H * (a.dev_hi - a.dev_lo) * a.B;
     if (blocks == 0) {
         // Nothing to launch: the events still mark this point of the stream.
-        if (start != nullptr && hipEventRecord(start, stream) != hipSuccess) return hipGetLastError();
-        if (stop != nullptr && hipEventRecord(stop, stream) != hipSuccess) return hipGetLastError();
-        return hipSuccess;
+        if (start != nullptr) {
+            const hipError_t e = hipEventRecord(start, stream);
+            if (e != hipSuccess) return e;
+        }
+        return stop != nullptr ? hipEventRecord(stop, stream) : hipSuccess;
     }
     // With events, the dispatch itself records them at the kernel's start and
     // end (no separate marker packets around the launch).

@@ -3,14 +3,23 @@
 // Striped layout: device d holds every N-th token, positions d, d+N, d+2N, ...
 // (Striped Attention summary page, "Summary" ¶2 and "Key points: Striped
 // layout"; the permutation is applied once before the model). In device
-// layout slot t = d*L + j holds position p = j*N + d, so
-//   forward gather:  y[o, t, :] = x[o, (t mod L)*N + t div L, :]
-//   inverse gather:  x[o, p, :] = y[o, (p mod N)*L + p div N, :]
-// Both are pure row gathers, HBM-bound: every byte is read once and written
-// once. Each thread moves 16-byte chunks; consecutive threads take
-// consecutive chunks of one row, so both the read and the write of a
-// wavefront cover contiguous row segments. Non-temporal hints keep the
-// streamed data from evicting other cache contents.
+// layout slot d*L + j holds position j*N + d, so
+//   forward gather:  y[o, d*L + j, :] = x[o, j*N + d, :]
+//   inverse gather:  x[o, j*N + d, :] = y[o, d*L + j, :]
+// Both are pure row copies, HBM-bound: every byte is read once and written
+// once.
+//
+// A workgroup owns a run of R consecutive tokens j0 .. j0+R-1 of one device d
+// (and one outer slice, grid y), so the device index and the first token
+// come from the block index once per workgroup, with no per-element
+// division by the sequence length or the device count. Within the run the
+// 256 threads take consecutive 16-byte chunks (4-byte words for rows that are
+// not a multiple of 16 bytes) of the R rows, eight per thread in flight
+// before any store; the chunk's row within the run is a division by the
+// chunks per row done with a multiply-high by a precomputed magic number.
+// Both the reads and the writes of a wavefront cover contiguous row
+// segments. Non-temporal hints keep the streamed data from evicting other
+// cache contents.
 #include "sra_internal.h"
 
 namespace sra {
@@ -18,93 +27,106 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-struct IndexMap {
-    uint32_t n_dev, L;
-    int n_shift, l_shift;   // log2 when a power of two, else -1
-    bool inverse;
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;                          // chunks per thread in flight
+constexpr uint32_t kRunChunks = kThreads * kUnroll; // chunks per workgroup pass
 
-    __device__ __forceinline__ uint32_t src_row(uint32_t t) const {
-        // t is the output row within one outer slice.
-        uint32_t a_div, a_mod;   // forward: t = d*L + j -> (d, j); inverse: p = j*N + d -> (j, d)
-        if (!inverse) {
-            if (l_shift >= 0) { a_div = t >> l_shift; a_mod = t & (L - 1); }
-            else { a_div = t / L; a_mod = t - a_div * L; }
-            return a_mod * n_dev + a_div;             // j*N + d
-        } else {
-            if (n_shift >= 0) { a_div = t >> n_shift; a_mod = t & (n_dev - 1); }
-            else { a_div = t / n_dev; a_mod = t - a_div * n_dev; }
-            return a_mod * L + a_div;                 // d*L + j
-        }
+// n / d for 32-bit n with an invariant divisor d (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (t + ((n - t) >> 1)) >> (l - 1), t = mulhi(m, n). l = 0 marks d = 1.
+struct Div32 {
+    uint32_t m;
+    int32_t l;
+    __device__ __forceinline__ uint32_t operator()(uint32_t n) const {
+        if (l == 0) return n;
+        const uint32_t t = __umulhi(m, n);
+        return (t + ((n - t) >> 1)) >> (l - 1);
     }
 };
 
-// Rows of 16-byte chunks; chunks per row = 1 << cpr_shift when cpr_shift >= 0.
-__global__ void __launch_bounds__(256) gather_rows16(const u32x4* __restrict__ x, u32x4* __restrict__ y,
-                                                     uint64_t total_chunks, uint32_t seq, uint32_t cpr,
-                                                     int cpr_shift, IndexMap map) {
-    uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total_chunks; c += stride) {
-        uint64_t row;
-        uint32_t chunk;
-        if (cpr_shift >= 0) { row = c >> cpr_shift; chunk = (uint32_t)(c & (cpr - 1)); }
-        else { row = c / cpr; chunk = (uint32_t)(c - row * cpr); }
-        uint64_t outer = row / seq;
-        uint32_t t = (uint32_t)(row - outer * seq);
-        uint64_t src = (outer * seq + map.src_row(t)) * cpr + chunk;
-        u32x4 v = __builtin_nontemporal_load(&x[src]);
-        __builtin_nontemporal_store(v, &y[c]);
+Div32 make_div32(uint32_t d) {
+    Div32 r{0u, 0};
+    if (d <= 1) return r;
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    r.l = l;
+    r.m = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+    return r;
+}
+
+// Copies the rows of token run (d, j0 .. j0+R-1) of outer slice blockIdx.y.
+// `cpr` elements of type T per row; `bpd` workgroups per device.
+template <typename T, bool kInverse>
+__global__ void __launch_bounds__(kThreads) gather_run(const T* __restrict__ x, T* __restrict__ y, uint32_t seq,
+                                                       uint32_t L, uint32_t N, uint32_t cpr, Div32 div_cpr,
+                                                       uint32_t R, uint32_t bpd) {
+    const uint32_t d = blockIdx.x / bpd;
+    const uint32_t j0 = (blockIdx.x - d * bpd) * R;
+    const uint32_t rows = min(R, L - j0);
+    const uint32_t total = rows * cpr;
+    const uint64_t slice = (uint64_t)blockIdx.y * seq * cpr;
+    // Source and destination row of local row r: device-layout slot d*L + j
+    // and position j*N + d.
+    const uint32_t dev_slot0 = d * L + j0;
+    const uint32_t pos0 = j0 * N + d;
+    for (uint32_t f0 = 0; f0 < total; f0 += kRunChunks) {
+        T v[kUnroll];
+        uint64_t dst[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t f = f0 + u * kThreads + threadIdx.x;
+            dst[u] = ~0ull;
+            if (f < total) {
+                const uint32_t r = div_cpr(f);
+                const uint32_t c = f - r * cpr;
+                const uint32_t slot = dev_slot0 + r, pos = pos0 + r * N;
+                const uint32_t src_row = kInverse ? slot : pos;
+                const uint32_t dst_row = kInverse ? pos : slot;
+                v[u] = __builtin_nontemporal_load(&x[slice + (uint64_t)src_row * cpr + c]);
+                dst[u] = slice + (uint64_t)dst_row * cpr + c;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (dst[u] != ~0ull) __builtin_nontemporal_store(v[u], &y[dst[u]]);
     }
 }
 
-// Same with 4-byte elements (rows whose size is not a multiple of 16 bytes).
-__global__ void __launch_bounds__(256) gather_rows4(const uint32_t* __restrict__ x, uint32_t* __restrict__ y,
-                                                    uint64_t total_words, uint32_t seq, uint32_t wpr,
-                                                    IndexMap map) {
-    uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total_words; c += stride) {
-        uint64_t row = c / wpr;
-        uint32_t w = (uint32_t)(c - row * wpr);
-        uint64_t outer = row / seq;
-        uint32_t t = (uint32_t)(row - outer * seq);
-        y[c] = x[(outer * seq + map.src_row(t)) * wpr + w];
+template <typename T>
+hipError_t launch_runs(const void* x, void* y, int64_t outer, int64_t seq, uint32_t cpr, int32_t n_dev, bool inverse,
+                       hipStream_t stream) {
+    const uint32_t L = (uint32_t)(seq / n_dev);
+    // Rows per workgroup: about kRunChunks chunks, at least one row.
+    const uint32_t R = cpr >= kRunChunks ? 1u : kRunChunks / cpr;
+    const uint32_t bpd = (L + R - 1) / R;
+    const Div32 dv = make_div32(cpr);
+    const uint64_t per_slice = (uint64_t)seq * cpr;
+    // Grid y carries the outer index, at most 65535 slices per launch.
+    for (int64_t o0 = 0; o0 < outer; o0 += 65535) {
+        const unsigned ny = (unsigned)(outer - o0 < 65535 ? outer - o0 : 65535);
+        const T* xs = (const T*)x + (uint64_t)o0 * per_slice;
+        T* ys = (T*)y + (uint64_t)o0 * per_slice;
+        const dim3 grid((unsigned)((uint64_t)n_dev * bpd), ny);
+        if (inverse)
+            hipLaunchKernelGGL((gather_run<T, true>), grid, dim3(kThreads), 0, stream, xs, ys, (uint32_t)seq, L,
+                               (uint32_t)n_dev, cpr, dv, R, bpd);
+        else
+            hipLaunchKernelGGL((gather_run<T, false>), grid, dim3(kThreads), 0, stream, xs, ys, (uint32_t)seq, L,
+                               (uint32_t)n_dev, cpr, dv, R, bpd);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-}
-
-int log2_exact(uint64_t v) {
-    if (v == 0 || (v & (v - 1))) return -1;
-    int s = 0;
-    while ((1ull << s) != v) ++s;
-    return s;
+    return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_permute(const void* x, void* y, int64_t outer, int64_t seq, int64_t row_bytes,
                           int32_t n_dev, bool inverse, hipStream_t stream) {
-    IndexMap map;
-    map.n_dev = (uint32_t)n_dev;
-    map.L = (uint32_t)(seq / n_dev);
-    map.n_shift = log2_exact(map.n_dev);
-    map.l_shift = log2_exact(map.L);
-    map.inverse = inverse;
-    const int threads = 256;
-    const uint64_t max_blocks = 256ull * 64;   // enough waves in flight on every CU; grid-stride beyond
-    if (row_bytes % 16 == 0 && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0)) {
-        uint32_t cpr = (uint32_t)(row_bytes / 16);
-        uint64_t total = (uint64_t)outer * seq * cpr;
-        uint64_t blocks = (total + threads - 1) / threads;
-        if (blocks > max_blocks) blocks = max_blocks;
-        hipLaunchKernelGGL(gather_rows16, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           (const u32x4*)x, (u32x4*)y, total, (uint32_t)seq, cpr, log2_exact(cpr), map);
-    } else {
-        uint32_t wpr = (uint32_t)(row_bytes / 4);
-        uint64_t total = (uint64_t)outer * seq * wpr;
-        uint64_t blocks = (total + threads - 1) / threads;
-        if (blocks > max_blocks) blocks = max_blocks;
-        hipLaunchKernelGGL(gather_rows4, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                           (const uint32_t*)x, (uint32_t*)y, total, (uint32_t)seq, wpr, map);
-    }
-    return hipGetLastError();
+    if (row_bytes % 16 == 0 && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0))
+        return launch_runs<u32x4>(x, y, outer, seq, (uint32_t)(row_bytes / 16), n_dev, inverse, stream);
+    return launch_runs<uint32_t>(x, y, outer, seq, (uint32_t)(row_bytes / 4), n_dev, inverse, stream);
 }
 
 }  // namespace sra

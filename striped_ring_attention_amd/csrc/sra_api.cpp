@@ -121,6 +121,32 @@ hipError_t launch_round(const sra_desc* d, const sra::RoundArgs& a, hipStream_t 
 
 int64_t elem_bytes(const sra_desc* d) { return d->dtype == SRA_DTYPE_BF16 ? 2 : 4; }
 
+// A byte range [p, p + bytes) named for error messages; bytes == 0 is empty.
+struct Span {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+bool overlap(const Span& a, const Span& b) {
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Written buffers must be disjoint from every read buffer and from each other.
+int check_disjoint(const Span* outs, int n_out, const Span* ins, int n_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j)
+            if (overlap(outs[i], ins[j]))
+                return fail(SRA_ERR_INVALID_ARG, "%s overlaps the input %s", outs[i].name, ins[j].name);
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(SRA_ERR_INVALID_ARG, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+    }
+    return SRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,6 +238,8 @@ static int permute_common(const void* src, void* dst, int64_t outer, int64_t seq
     if (src == nullptr || dst == nullptr) return fail(SRA_ERR_INVALID_ARG, "null tensor pointer");
     if (outer < 1) return fail(SRA_ERR_INVALID_ARG, "outer must be >= 1");
     if (row_bytes < 4 || row_bytes % 4 != 0) return fail(SRA_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 4");
+    // The gather indexes the elements of one row with 32 bits.
+    if (row_bytes > ((int64_t)1 << 31)) return fail(SRA_ERR_INVALID_ARG, "row_bytes must be <= 2^31");
     if (((uintptr_t)src & 3u) || ((uintptr_t)dst & 3u)) return fail(SRA_ERR_INVALID_ARG, "tensors must be 4-byte aligned");
     const double total = (double)outer * (double)seq * (double)row_bytes;
     if (total > 4.0e18) return fail(SRA_ERR_INVALID_ARG, "tensor too large");
@@ -292,13 +320,16 @@ int sra_ring_attn_fwd(const sra_desc* desc, const void* q, const void* k, const 
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(SRA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     if (need > 0 && !aligned16(workspace)) return fail(SRA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    // Overlap between inputs and outputs would corrupt inputs that later rounds read.
-    const uintptr_t nbytes = (uintptr_t)(desc->batch * desc->seq * desc->heads * desc->head_dim * elem_bytes(desc));
-    const uintptr_t o0 = (uintptr_t)o, o1 = o0 + nbytes;
-    for (const void* in : {q, k, v}) {
-        const uintptr_t i0 = (uintptr_t)in, i1 = i0 + nbytes;
-        if (i0 < o1 && o0 < i1) return fail(SRA_ERR_INVALID_ARG, "o overlaps an input");
-    }
+    // Every buffer the driver writes (o, lse, the workspace) is written while
+    // later rounds still read q, k and v, and the per-round schedule reads its
+    // accumulator back: no written buffer may overlap an input or another
+    // written buffer.
+    const size_t nbytes = (size_t)(desc->batch * desc->seq * desc->heads * desc->head_dim * elem_bytes(desc));
+    const size_t lbytes = (size_t)(desc->batch * desc->seq * desc->heads) * sizeof(float);
+    const Span outs[3] = {{o, nbytes, "o"}, {lse, lbytes, "lse"}, {workspace, need, "workspace"}};
+    const Span ins[3] = {{q, nbytes, "q"}, {k, nbytes, "k"}, {v, nbytes, "v"}};
+    st = check_disjoint(outs, 3, ins, 3);
+    if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     sra::RoundArgs a = make_args(desc, q, k, v);
     a.live_counts = live_counts;
@@ -351,17 +382,15 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
     if (workspace == nullptr || workspace_bytes < need)
         return fail(SRA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     if ((uintptr_t)workspace & 15u) return fail(SRA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    // Outputs must not overlap the inputs the kernels read.
-    const uintptr_t nbytes = (uintptr_t)(desc->batch * desc->seq * desc->heads * desc->head_dim * 2);
-    for (const void* out : std::initializer_list<const void*>{dq, dk, dv}) {
-        const uintptr_t a0 = (uintptr_t)out, a1 = a0 + nbytes;
-        for (const void* in : std::initializer_list<const void*>{q, k, v, o, dout}) {
-            const uintptr_t b0 = (uintptr_t)in, b1 = b0 + nbytes;
-            if (a0 < b1 && b0 < a1) return fail(SRA_ERR_INVALID_ARG, "a gradient overlaps an input");
-        }
-        const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + need;
-        if (a0 < w1 && w0 < a1) return fail(SRA_ERR_INVALID_ARG, "a gradient overlaps the workspace");
-    }
+    // The gradients and the workspace (written by the first kernel, read by
+    // the later ones) must not overlap any input or one another.
+    const size_t nbytes = (size_t)(desc->batch * desc->seq * desc->heads * desc->head_dim * 2);
+    const size_t lbytes = (size_t)(desc->batch * desc->seq * desc->heads) * sizeof(float);
+    const Span outs[4] = {{dq, nbytes, "dq"}, {dk, nbytes, "dk"}, {dv, nbytes, "dv"}, {workspace, need, "workspace"}};
+    const Span ins[6] = {{q, nbytes, "q"}, {k, nbytes, "k"}, {v, nbytes, "v"},
+                         {o, nbytes, "o"}, {dout, nbytes, "dout"}, {lse, lbytes, "lse"}};
+    st = check_disjoint(outs, 4, ins, 6);
+    if (st) return st;
     sra::BwdArgs a{};
     a.q = q;
     a.k = k;

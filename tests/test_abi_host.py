@@ -179,10 +179,52 @@ def test_invalid_fwd_arguments_rejected(lib):
     assert fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE2, ctypes.c_void_p(1 << 40), need, None, None,
                None) == INVALID                                      # o aliases q
     assert fwd(ctypes.byref(desc(seq=63)), FAKE, FAKE, FAKE, FAKE2, FAKE2, None, 0, None, None, None) == INVALID
+    # every written buffer (o, lse, workspace) must be disjoint from q, k, v and from each other
+    O, LSE, WS = ctypes.c_void_p(1 << 32), ctypes.c_void_p(1 << 34), ctypes.c_void_p(1 << 36)
+    assert fwd(ctypes.byref(d), FAKE, FAKE, FAKE, O, ctypes.c_void_p((1 << 20) + 64), WS, need, None, None,
+               None) == INVALID                                      # lse inside q
+    assert b"lse" in lib.sra_last_error()
+    assert fwd(ctypes.byref(d), FAKE, FAKE2, FAKE, O, LSE, ctypes.c_void_p((1 << 30) + 4096), need, None, None,
+               None) == INVALID                                      # workspace inside k
+    assert b"workspace" in lib.sra_last_error()
+    assert fwd(ctypes.byref(d), FAKE, FAKE, FAKE, O, ctypes.c_void_p((1 << 32) + 256), WS, need, None, None,
+               None) == INVALID                                      # lse inside o
+    assert fwd(ctypes.byref(d), FAKE, FAKE, FAKE, O, LSE, ctypes.c_void_p((1 << 34) + 16), need, None, None,
+               None) == INVALID                                      # workspace overlaps lse
+    assert b"overlap" in lib.sra_last_error()
     d1 = desc(n_dev=1)
     assert lib.sra_fwd_workspace_bytes(ctypes.byref(d1)) == 0
     df = desc(dtype=sra.DTYPE_F32, head_dim=64)
     assert lib.sra_fwd_workspace_bytes(ctypes.byref(df)) == 0
+
+
+def test_invalid_bwd_arguments_rejected(lib):
+    d = desc()
+    need = lib.sra_bwd_workspace_bytes(ctypes.byref(d))
+    assert need == 1 * 64 * 2 * 2 * 4
+    bwd = lib.sra_ring_attn_bwd
+    Q, K, V, O, LSE, DO = (ctypes.c_void_p(1 << s) for s in (20, 22, 24, 26, 28, 30))
+    DQ, DK, DV, WS = (ctypes.c_void_p(1 << s) for s in (32, 34, 36, 38))
+
+    def call(dd=d, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=LSE, do=DO, dq=DQ, dk=DK, dv=DV, ws=WS, n=need)
+        a.update(kw)
+        return bwd(ctypes.byref(dd), a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                   a["ws"], a["n"], None)
+
+    assert call(dd=desc(dtype=sra.DTYPE_F32, head_dim=64)) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(n=need - 1) == WORKSPACE
+    assert call(dq=None) == INVALID
+    assert call(dk=ctypes.c_void_p((1 << 34) + 8)) == INVALID                  # misaligned
+    assert call(dq=ctypes.c_void_p((1 << 20) + 4096)) == INVALID               # dq inside q
+    assert call(ws=ctypes.c_void_p((1 << 26) + 64)) == INVALID                 # workspace inside o
+    assert b"workspace" in lib.sra_last_error()
+    assert call(ws=ctypes.c_void_p((1 << 28) + 16)) == INVALID                 # workspace inside lse
+    assert call(dv=ctypes.c_void_p((1 << 28) + 16)) == INVALID                 # dv inside lse
+    assert call(ws=ctypes.c_void_p((1 << 36) + 16)) == INVALID                 # workspace inside dv
+    assert call(dk=DQ) == INVALID                                              # two gradients alias
+    assert b"overlap" in lib.sra_last_error()
 
 
 def test_invalid_permute_and_merge_rejected(lib):
@@ -190,6 +232,7 @@ def test_invalid_permute_and_merge_rejected(lib):
     assert P(FAKE, FAKE2, 1, 63, 256, 4, None) == INVALID          # seq % n_dev
     assert P(FAKE, FAKE2, 1, 64, 6, 4, None) == INVALID            # row_bytes % 4
     assert P(FAKE, FAKE2, 0, 64, 256, 4, None) == INVALID          # outer
+    assert P(FAKE, FAKE2, 1, 64, (1 << 31) + 4, 4, None) == INVALID   # row too wide for 32-bit element offsets
     assert P(None, FAKE2, 1, 64, 256, 4, None) == INVALID
     assert P(FAKE, ctypes.c_void_p((1 << 20) + 100), 1, 64, 256, 4, None) == INVALID   # overlap
     assert lib.sra_unstripe(FAKE, FAKE2, 1, 64, 256, 0, None) == INVALID

@@ -58,6 +58,9 @@ def maxabs(a, b):
     ((1, 1536, 32, 128), torch.bfloat16, 16),    # 8 KiB rows, N = 16
     ((3, 48, 2, 8), torch.bfloat16, 48),         # N = S
     ((1, 7, 4), torch.float32, 1),               # N = 1 (identity)
+    ((1, 1536, 3, 4096), torch.bfloat16, 16),    # 24 KiB rows (one row per workgroup), L = 96
+    ((2, 3072, 32, 128), torch.bfloat16, 3),     # N = 3, batch 2
+    ((1, 393216, 1, 8), torch.float32, 16),      # 32-byte rows, L = 24,576 (not a power of two)
 ])
 def test_permute_bit_exact(sra, shape, dtype, n_dev):
     say("permute", shape, dtype, n_dev)
@@ -225,20 +228,28 @@ def sampled_rows(S, N, n_random, seed):
 
 @pytest.mark.slow
 def test_fwd_mid_bf16_sampled_rows(sra):
+    """Mid (65,536 tokens, 32 heads, 8 devices): sampled rows on every head
+    against the oracle, for the per-round schedule in both layouts and for
+    the benchmark's launch (fused, striped, original order)."""
     w = WORKLOADS["mid"]
     x = make_inputs("mid", device="cuda")
-    heads = [0, 17, 31]
     rows = sampled_rows(w["seq"], w["n_dev"], 24, 5)
-    cpu = {n: x[n][:, :, heads].cpu().double().numpy() for n in ("q", "k", "v")}
+    cpu = {n: x[n][:, :int(rows.max()) + 1].cpu() for n in ("q", "k", "v")}
     o_ref, l_ref = oracle.attention_rows(cpu["q"], cpu["k"], cpu["v"], rows)
+    say(f"mid: {len(rows)} sampled rows x {w['heads']} heads")
     for layout in LAYOUTS:
         o, lse, counts = run_full(sra, x, w["n_dev"], layout)
-        og = np64(o[:, rows][:, :, heads])
-        lg = np64(lse[:, rows][:, :, heads])
-        e_o, e_l = maxabs(og, o_ref), maxabs(lg, l_ref)
+        e_o, e_l = maxabs(np64(o[:, rows]), o_ref), maxabs(np64(lse[:, rows]), l_ref)
         say(f"mid layout={layout}: sampled O {e_o:.3g} LSE {e_l:.3g}")
         assert e_o <= 2e-2 and e_l <= 2e-2
         assert torch.equal(counts, _census(sra, w["seq"], w["n_dev"], layout, torch.bfloat16, w["heads"]))
+    o, lse = sra.ring_attn_fwd(x["q"], x["k"], x["v"], w["n_dev"], oracle.STRIPED, schedule=sra.SCHEDULE_FUSED,
+                               order=sra.ORDER_ORIGINAL)
+    torch.cuda.synchronize()
+    e_o, e_l = maxabs(np64(o[:, rows]), o_ref), maxabs(np64(lse[:, rows]), l_ref)
+    say(f"mid fused original order: sampled O {e_o:.3g} LSE {e_l:.3g}")
+    assert e_o <= 2e-2 and e_l <= 2e-2
+    assert torch.equal(o[:, 0], x["v"][:, 0])
 
 
 @pytest.mark.slow
