@@ -263,6 +263,23 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k,
                       const void* dout, void* dq, void* dk, void* dv,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* sra_ring_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The per-row statistics go to an array
+ * the library holds on each GPU it runs on (256 MiB, kept until the process
+ * ends), so batch * seq * heads must be at most 33,554,432 rows; a larger
+ * descriptor returns SRA_ERR_WORKSPACE before any work is enqueued. The
+ * call makes no allocation; its first call on a device (the current device)
+ * looks up the array's address there. Every call on one GPU uses that GPU's
+ * one array: calls that overlap in time on the same GPU (other streams, other
+ * threads) race and give undefined results; calls on one stream are
+ * ordered. Arguments, results and errors are otherwise those of
+ * sra_ring_attn_bwd (same kernels, bit-identical outputs). */
+int sra_ring_attn_bwd_noalloc(const sra_desc* desc, const void* q,
+                              const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq,
+                              void* dk, void* dv, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

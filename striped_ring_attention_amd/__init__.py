@@ -66,6 +66,8 @@ _PROTOS = {
     "sra_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SraDesc)]),
     "sra_ring_attn_bwd": (_i32, [ctypes.POINTER(SraDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_size_t, _vp]),
+    "sra_ring_attn_bwd_noalloc": (_i32, [ctypes.POINTER(SraDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp]),
 }
 
 
@@ -279,6 +281,17 @@ def ring_attn_bwd(q, k, v, o, lse, dout, n_dev, layout, scale=0.0, dq=None, dk=N
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().sra_ring_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream()))
+    return dq, dk, dv
+
+
+def ring_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, n_dev, layout, scale=0.0, order=ORDER_DEVICE):
+    """ring_attn_bwd into caller-given dq, dk, dv with no workspace: the
+    library's own per-GPU statistics array is used, and nothing is allocated
+    (calls overlapping in time on one GPU race)."""
+    _check_tensors(q, k, v, o, lse, dout, dq, dk, dv)
+    d = _desc_for(q, n_dev, layout, scale, order=order)
+    _check(lib().sra_ring_attn_bwd_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                           _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream()))
     return dq, dk, dv
 
 

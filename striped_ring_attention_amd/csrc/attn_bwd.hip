@@ -37,9 +37,18 @@
 // No atomics: each gradient accumulates in the registers of the workgroup
 // that owns its rows, so results are deterministic. S and dP are computed in
 // both kernels (seven tile products per live tile instead of five).
+#include <mutex>
+
 #include "kernel_common.h"
 
 namespace sra {
+
+// Backward statistics storage for callers that cannot allocate: one array
+// per GPU, held by the library for the life of the process. Host code never
+// passes `scratch` itself (in host code that name is only a stand-in for the
+// symbol); it passes the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[kBwdScratchBytes / sizeof(float)];
+
 namespace {
 
 using namespace kc;
@@ -320,6 +329,28 @@ __global__ void __launch_bounds__(DQ_NT, 1) bwd_dq(BwdArgs a) {
 }
 
 }  // namespace
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and cached.
+hipError_t bwd_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // The dK/dV kernel lives in attn_bwd_dkdv.hip (built with its own flags).
 hipError_t launch_bwd_dkdv_bf16_d128(const BwdArgs& a, hipStream_t stream);

@@ -364,9 +364,15 @@ size_t sra_bwd_workspace_bytes(const sra_desc* desc) {
     return (size_t)(desc->batch * desc->seq * desc->heads) * 2 * sizeof(float);
 }
 
-int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const void* v, const void* o,
-                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the two backward entry points; `workspace` null with
+// need_ws false skips the workspace checks (the allocation-free form uses the
+// library's own array).
+int bwd_check(const sra_desc* desc, const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, bool need_ws) {
     int st = check_desc(desc);
     if (st) return st;
     if (desc->dtype != SRA_DTYPE_BF16)
@@ -379,18 +385,24 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
         if (!aligned16(p)) return fail(SRA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
     if ((uintptr_t)lse & 3u) return fail(SRA_ERR_INVALID_ARG, "lse misaligned");
     const size_t need = sra_bwd_workspace_bytes(desc);
-    if (workspace == nullptr || workspace_bytes < need)
-        return fail(SRA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-    if ((uintptr_t)workspace & 15u) return fail(SRA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (need_ws) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(SRA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+        if ((uintptr_t)workspace & 15u) return fail(SRA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
     // The gradients and the workspace (written by the first kernel, read by
     // the later ones) must not overlap any input or one another.
     const size_t nbytes = (size_t)(desc->batch * desc->seq * desc->heads * desc->head_dim * 2);
     const size_t lbytes = (size_t)(desc->batch * desc->seq * desc->heads) * sizeof(float);
-    const Span outs[4] = {{dq, nbytes, "dq"}, {dk, nbytes, "dk"}, {dv, nbytes, "dv"}, {workspace, need, "workspace"}};
+    const Span outs[4] = {{dq, nbytes, "dq"}, {dk, nbytes, "dk"}, {dv, nbytes, "dv"},
+                          {need_ws ? workspace : nullptr, need, "workspace"}};
     const Span ins[6] = {{q, nbytes, "q"}, {k, nbytes, "k"}, {v, nbytes, "v"},
                          {o, nbytes, "o"}, {dout, nbytes, "dout"}, {lse, lbytes, "lse"}};
-    st = check_disjoint(outs, 4, ins, 6);
-    if (st) return st;
+    return check_disjoint(outs, 4, ins, 6);
+}
+
+sra::BwdArgs bwd_args(const sra_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, float* stats) {
     sra::BwdArgs a{};
     a.q = q;
     a.k = k;
@@ -398,7 +410,7 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
     a.o = o;
     a.lse = lse;
     a.dout = dout;
-    a.stats = (float*)workspace;
+    a.stats = stats;
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
@@ -411,6 +423,37 @@ int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const 
     a.strided = desc->order == SRA_ORDER_ORIGINAL && desc->layout == SRA_LAYOUT_STRIPED;
     a.scale = eff_scale(desc);
     a.scale_log2 = (float)((double)a.scale * 1.4426950408889634074);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sra_ring_attn_bwd(const sra_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    const int st = bwd_check(desc, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, true);
+    if (st) return st;
+    const sra::BwdArgs a = bwd_args(desc, q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace);
+    return hip_status(sra::launch_bwd_bf16_d128(a, (hipStream_t)stream), "ring backward launch");
+}
+
+int sra_ring_attn_bwd_noalloc(const sra_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv, void* stream) {
+    const int st = bwd_check(desc, q, k, v, o, lse, dout, dq, dk, dv, nullptr, 0, false);
+    if (st) return st;
+    const size_t need = sra_bwd_workspace_bytes(desc);
+    if (need > sra::kBwdScratchBytes)
+        return fail(SRA_ERR_WORKSPACE,
+                    "batch * seq * heads = %lld rows need %zu bytes of statistics; the allocation-free backward "
+                    "holds %zu bytes (at most %zu rows)",
+                    (long long)(desc->batch * desc->seq * desc->heads), need, sra::kBwdScratchBytes,
+                    sra::kBwdScratchBytes / 8);
+    void* stats = nullptr;
+    const hipError_t e = sra::bwd_scratch(&stats);
+    if (e != hipSuccess) return hip_status(e, "scratch address lookup");
+    const sra::BwdArgs a = bwd_args(desc, q, k, v, o, lse, dout, dq, dk, dv, (float*)stats);
     return hip_status(sra::launch_bwd_bf16_d128(a, (hipStream_t)stream), "ring backward launch");
 }
 

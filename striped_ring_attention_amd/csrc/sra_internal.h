@@ -85,6 +85,13 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream);
+
+// Bytes of the library-held backward statistics array (one per GPU): 8 bytes
+// per (b, s, h) row, so at most 33,554,432 rows.
+constexpr size_t kBwdScratchBytes = (size_t)256 << 20;
+// Device address of that array on the current device (looked up on the
+// first call per device).
+hipError_t bwd_scratch(void** ptr);
 hipError_t launch_round_f32(const RoundArgs& a, int64_t head_dim, hipStream_t stream);
 
 hipError_t launch_permute(const void* x, void* y, int64_t outer, int64_t seq, int64_t row_bytes,

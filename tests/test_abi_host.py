@@ -227,6 +227,23 @@ def test_invalid_bwd_arguments_rejected(lib):
     assert b"overlap" in lib.sra_last_error()
 
 
+def test_noalloc_bwd_validation(lib):
+    """The allocation-free backward validates like the workspace form and
+    rejects problems larger than its library-held array before any HIP call."""
+    nb = lib.sra_ring_attn_bwd_noalloc
+    Q, K, V, O, LSE, DO = (ctypes.c_void_p(1 << s) for s in (20, 22, 24, 26, 28, 30))
+    DQ, DK, DV = (ctypes.c_void_p(1 << s) for s in (32, 34, 36))
+    big = desc(seq=1 << 25, heads=2, n_dev=1024)          # 67,108,864 rows > 33,554,432
+    far = [ctypes.c_void_p((i + 1) << 38) for i in range(9)]   # 16 GiB tensors, disjoint
+    assert nb(ctypes.byref(big), *far, None) == WORKSPACE
+    assert b"allocation-free" in lib.sra_last_error()
+    d = desc()
+    assert nb(ctypes.byref(d), Q, K, V, O, LSE, DO, None, DK, DV, None) == INVALID
+    assert nb(ctypes.byref(d), Q, K, V, O, LSE, DO, ctypes.c_void_p((1 << 20) + 256), DK, DV, None) == INVALID
+    assert nb(ctypes.byref(desc(dtype=sra.DTYPE_F32, head_dim=64)), Q, K, V, O, LSE, DO, DQ, DK, DV,
+              None) == UNSUPPORTED
+
+
 def test_invalid_permute_and_merge_rejected(lib):
     P = lib.sra_stripe_permute
     assert P(FAKE, FAKE2, 1, 63, 256, 4, None) == INVALID          # seq % n_dev
