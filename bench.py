@@ -1,12 +1,14 @@
 """Benchmark: striped ring-attention forward on one MI355X.
 
 One step = original-order Q, K, V -> striped device layout -> all N ring
-rounds -> O and LSE back in original order. By default (--order original)
-that is one launch: the ring kernel addresses device d's j-th token at its
-position j*N + d, so the stripe permutation and its inverse are folded into
-its row addressing. With --order device the step runs the explicit gather
-kernels (stripe_permute Q, K, V; ring on device-layout tensors; unstripe O
-and LSE); that variant is timed alongside either way. Inputs are resident in
+rounds -> O and LSE back in original order. With --order device (the default
+at 262,144 and 786,432 tokens) the step runs the explicit gather kernels:
+stripe_permute Q, K, V; the ring on device-layout tensors, each device's
+stripe contiguous as on a real ring; unstripe O and LSE. With --order
+original (the default at the shorter lengths) it is one launch: the ring
+kernel addresses device d's j-th token at its position j*N + d, so the
+stripe permutation and its inverse are folded into its row addressing. The
+other form is timed alongside either way. Inputs are resident in
 HBM before the timed region. The ring runs with the fused schedule by
 default (one launch walks every (round, key tile) pair, the log-sum-exp
 merge done online); the per-round schedule (one launch per ring round, merge
@@ -63,6 +65,11 @@ TRAFFIC = [
      "bytes_per_launch": 161893422,
      "fetch_bytes_per_launch": 124151245, "write_bytes_per_launch": 37742177,
      "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99992}},
+    {"workload": "very_long", "order": "device",
+     "kernel_sources_sha256": "d957267665a42affdd6c6fe1bba01e5442b9573004ab3263322fd86f3b7f7d12",
+     "bytes_per_launch": 6177997644382,
+     "fetch_bytes_per_launch": 6170728382114, "write_bytes_per_launch": 7269262267,
+     "copy_scale": {"FETCH_SIZE": 1.99999, "WRITE_SIZE": 1.00000}},
 ]
 
 
@@ -81,10 +88,11 @@ def parse():
     ap.add_argument("--layout", default="striped", choices=["striped", "contiguous"])
     ap.add_argument("--schedule", default="fused", choices=["fused", "per_round"],
                     help="ring schedule of the timed step (the other one is timed alongside)")
-    ap.add_argument("--order", default="original", choices=["original", "device"],
+    ap.add_argument("--order", default=None, choices=["original", "device"],
                     help="original: q, k, v, o, lse in token order, the stripe permutation folded into the ring "
                          "kernel's row addressing (one launch per step); device: gather into the striped "
-                         "device layout, ring, gather back (the other one is timed alongside)")
+                         "device layout, ring, gather back (the other one is timed alongside). Default per "
+                         "workload: device for Long and Very long, original otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--sec-steps", type=int, default=None,
@@ -109,6 +117,12 @@ DEFAULT_STEPS = {"short": (300, 300), "mid": (10, 4), "long": (3, 1), "very_long
 SECONDARY_CAP = {"short": 300, "mid": 10, "long": 3, "very_long": 2}
 BACKWARD_CAP = {"short": 100, "mid": 10, "long": 3, "very_long": 2}
 RING_SIM_REPS = {"long": 1, "very_long": 1}
+# Default order of the timed step. At 262,144 and 786,432 tokens the ring
+# kernel on device-layout tensors (each device's stripe contiguous, as on a
+# real ring) runs ~2% faster than with the stripe read in place, which more
+# than pays for the explicit gathers (~10 ms of a ~4.4 s step at 786,432
+# tokens); at the shorter lengths the gathers cost more than they save.
+DEFAULT_ORDER = {"long": "device", "very_long": "device"}
 WARM_SECONDS = 0.15   # back-to-back work before each secondary timed section
 
 
@@ -359,6 +373,8 @@ def main():
     def launches(sc):
         return N if sc == sra.SCHEDULE_PER_ROUND else 1
 
+    if args.order is None:
+        args.order = DEFAULT_ORDER.get(args.workload, "original")
     ordr = sra.ORDER_ORIGINAL if args.order == "original" else sra.ORDER_DEVICE
 
     def step(lay, sc, events=None, perm_events=None, cnt=None, od=None):
@@ -435,16 +451,21 @@ def main():
     else:
         flops_per_launch = [useful_flops]
 
-    # The explicit gather kernels (device order, striped): the timed step itself
-    # when --order device, else a run of its own.
+    # The other order, timed alongside (striped): the explicit gather kernels
+    # are timed inside the device-order step (the timed step itself when
+    # --order device, else a run of its own).
     perm = {}
-    dev_step = None
-    if layout == sra.STRIPED and not dev_striped:
-        warm(torch, lambda: step(layout, sched, od=sra.ORDER_DEVICE))
-        d_step, d_launch, perm_ev = timed(layout, sched, sec_K, perm=True, od=sra.ORDER_DEVICE)
-        d_attn = sum(sum(p) for p in d_launch) / sec_K
-        dev_step = {"step_ms": d_step, "step_useful_TFLOPs": useful_flops / (d_step * 1e-3) / 1e12,
-                    "ring_ms": d_attn, "ring_useful_TFLOPs": useful_flops / (d_attn * 1e-3) / 1e12}
+    other_step = None
+    if layout == sra.STRIPED:
+        other = sra.ORDER_ORIGINAL if dev_striped else sra.ORDER_DEVICE
+        warm(torch, lambda: step(layout, sched, od=other))
+        o_step, o_launch, o_perm = timed(layout, sched, sec_K, perm=not dev_striped, od=other)
+        if not dev_striped:
+            perm_ev = o_perm
+        o_attn = sum(sum(p) for p in o_launch) / sec_K
+        other_step = {"step_ms": o_step, "step_useful_TFLOPs": useful_flops / (o_step * 1e-3) / 1e12,
+                      "ring_ms": o_attn, "ring_useful_TFLOPs": useful_flops / (o_attn * 1e-3) / 1e12,
+                      "steps": sec_K}
     if layout == sra.STRIPED:
         n_ev = len(perm_ev)
         p_ms = sum(perm_ev[i][0].elapsed_time(perm_ev[i][1]) for i in range(n_ev)) / n_ev
@@ -456,7 +477,7 @@ def main():
                 "unstripe_o_lse_ms": u_ms, "unstripe_GBps": u_bytes / (u_ms * 1e-3) / 1e9,
                 "hbm_peak_GBps": PEAK_HBM_GBS, "note": "timed back to back inside the step (caches warm)"}
 
-    note("device-order step done")
+    note("other-order step done")
     # Cold-cache rates: the 256 MB Infinity Cache is flushed (a 1 GiB write)
     # before each repetition; median of 5.
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.device)
@@ -552,8 +573,9 @@ def main():
             note(f"compare {cname} done")
         compare[f"{args.layout}_{args.schedule}"] = {"ring_ms": attn_ms, "ring_useful_TFLOPs": attn_tflops,
                                                      "step_ms": ms_step}
-        if dev_step is not None:
-            compare[f"{args.layout}_{args.schedule}_device_order"] = dev_step
+        if other_step is not None:
+            oname = "original" if dev_striped else "device"
+            compare[f"{args.layout}_{args.schedule}_{oname}_order"] = other_step
 
     critical = None
     if not args.no_critical_path:

@@ -61,6 +61,8 @@ def maxabs(a, b):
     ((1, 1536, 3, 4096), torch.bfloat16, 16),    # 24 KiB rows (one row per workgroup), L = 96
     ((2, 3072, 32, 128), torch.bfloat16, 3),     # N = 3, batch 2
     ((1, 393216, 1, 8), torch.float32, 16),      # 32-byte rows, L = 24,576 (not a power of two)
+    ((1, 786432, 32, 128), torch.bfloat16, 16),  # Very long Q/K/V (6.4 GB): the large-tensor launch shape
+    ((1, 393216, 3, 60), torch.float32, 16),     # 720-byte rows, 283 MB: 4-byte path, large-tensor shape
 ])
 def test_permute_bit_exact(sra, shape, dtype, n_dev):
     say("permute", shape, dtype, n_dev)
