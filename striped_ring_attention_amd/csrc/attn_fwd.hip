@@ -87,6 +87,7 @@ constexpr int BN = kBf16TileK;   // 64 keys per tile
 constexpr int NT = 512;          // 8 wavefronts in two groups of 4: one wave of each group per SIMD
 constexpr int NS = 4;             // K/V tile stages in LDS
 constexpr float kTau = 8.0f;     // lazy-rescale threshold (log2 units)
+constexpr float kSumCap = 256.0f;  // 2^kTau: a lane's weights sum past this only if one of them does
 
 static_assert(BM == 256 && BN == 64 && NT == 512 && D == 128, "thread mappings below assume these");
 
@@ -236,7 +237,9 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     f32x16 oacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;   // running offset (log2 domain), equal in both halves
+    // Running offset (log2 domain), equal in both halves. Rows past the end
+    // are fully masked; they start at offset 0 so they never ask for the max.
+    float m_run = row_ok ? -INFINITY : 0.f;
     float l_part = 0.f;        // this half's share of the row sum
     const float sl = a.scale_log2;
 
@@ -343,31 +346,43 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
             for (int i = 0; i < 16; ++i)
                 if (8 * (i >> 2) + (i & 3) + 32 >= lim) sacc[1][i] = -INFINITY;
         }
-        float mx = fmaxf(fmaxf(sacc[0][0], sacc[1][0]), sacc[0][1]);
+        // Weights against the current offset first. Only when some weight of
+        // the wave exceeds 2^kTau (its lane's partial sum then does too), or a
+        // row has no offset yet, does the wave take the exact path below: the
+        // row max, the raised offset and the weights again. Otherwise the
+        // offset stays, exactly as the max test would have decided.
+        float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float ls0, ls1;
+        auto weights = [&]() {
 #pragma unroll
-        for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[1][i]), fmaxf(sacc[0][i + 1], sacc[1][i + 1]));
-        mx = fmaxf(fmaxf(mx, sacc[1][15]), sacc[0][15]);
-        const float m_tile = halves_max(mx) * sl;   // raw max times scale (> 0 keeps the order)
-        const bool need = m_tile > m_run + kTau;
-        // The O rescale this implies is applied in the next MFMA phase, just
-        // before this tile's P V is accumulated (keeps O's registers in place).
-        resc = __builtin_amdgcn_ballot_w64(need) != 0;
-        {
+            for (int i = 0; i < 16; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], sl, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], sl, -m_use));
+                ls0 = i == 0 ? p0 : ls0 + p0;
+                ls1 = i == 0 ? p1 : ls1 + p1;
+                pop[0][i >> 3][i & 7] = (bf16)p0;
+                pop[1][i >> 3][i & 7] = (bf16)p1;
+            }
+        };
+        weights();
+        const bool check = !(ls0 + ls1 <= kSumCap) || m_run == -INFINITY;
+        resc = false;
+        if (__builtin_amdgcn_ballot_w64(check) != 0) {
+            float mx = fmaxf(fmaxf(sacc[0][0], sacc[1][0]), sacc[0][1]);
+#pragma unroll
+            for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[1][i]), fmaxf(sacc[0][i + 1], sacc[1][i + 1]));
+            mx = fmaxf(fmaxf(mx, sacc[1][15]), sacc[0][15]);
+            const float m_tile = halves_max(mx) * sl;   // raw max times scale (> 0 keeps the order)
+            const bool need = m_tile > m_run + kTau;
+            // The O rescale this implies is applied in the next MFMA phase, just
+            // before this tile's P V is accumulated (keeps O's registers in place).
+            resc = __builtin_amdgcn_ballot_w64(need) != 0;
             const float m_new = need ? fmaxf(m_run, m_tile) : m_run;
             alpha_p = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_part *= alpha_p;
             m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float ls0, ls1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], sl, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], sl, -m_use));
-            ls0 = i == 0 ? p0 : ls0 + p0;
-            ls1 = i == 0 ? p1 : ls1 + p1;
-            pop[0][i >> 3][i & 7] = (bf16)p0;
-            pop[1][i >> 3][i & 7] = (bf16)p1;
+            m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            weights();
         }
         l_part += ls0 + ls1;
     };
