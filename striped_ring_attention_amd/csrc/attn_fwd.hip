@@ -39,6 +39,8 @@
 //    patterns are bank-conflict-free.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "kernel_common.h"
 
 namespace sra {
@@ -241,6 +243,8 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     // are fully masked; they start at offset 0 so they never ask for the max.
     float m_run = row_ok ? -INFINITY : 0.f;
     float l_part = 0.f;        // this half's share of the row sum
+    float neg_m = 0.f;         // minus the offset the weights are taken against (0 while it is unset)
+    bool rows_set = false;     // every row of the wave has an offset (wave-uniform)
     const float sl = a.scale_log2;
 
     // K/V staging: each tile is loaded straight into LDS (buffer_load ...
@@ -347,17 +351,17 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
                 if (8 * (i >> 2) + (i & 3) + 32 >= lim) sacc[1][i] = -INFINITY;
         }
         // Weights against the current offset first. Only when some weight of
-        // the wave exceeds 2^kTau (its lane's partial sum then does too), or a
-        // row has no offset yet, does the wave take the exact path below: the
-        // row max, the raised offset and the weights again. Otherwise the
-        // offset stays, exactly as the max test would have decided.
-        float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        // the wave exceeds 2^kTau (its lane's partial sum then does too), or
+        // some row of the wave has no offset yet, does the wave take the exact
+        // path below: the row max, the raised offset and the weights again.
+        // Otherwise the offset stays, exactly as the max test would have
+        // decided.
         float ls0, ls1;
         auto weights = [&]() {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], sl, -m_use));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], sl, -m_use));
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], sl, neg_m));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], sl, neg_m));
                 ls0 = i == 0 ? p0 : ls0 + p0;
                 ls1 = i == 0 ? p1 : ls1 + p1;
                 pop[0][i >> 3][i & 7] = (bf16)p0;
@@ -365,9 +369,8 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
             }
         };
         weights();
-        const bool check = !(ls0 + ls1 <= kSumCap) || m_run == -INFINITY;
         resc = false;
-        if (__builtin_amdgcn_ballot_w64(check) != 0) {
+        if (!rows_set || __builtin_amdgcn_ballot_w64(!(ls0 + ls1 <= kSumCap)) != 0) {
             float mx = fmaxf(fmaxf(sacc[0][0], sacc[1][0]), sacc[0][1]);
 #pragma unroll
             for (int i = 1; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sacc[1][i]), fmaxf(sacc[0][i + 1], sacc[1][i + 1]));
@@ -381,7 +384,8 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
             alpha_p = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_part *= alpha_p;
             m_run = m_new;
-            m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+            rows_set = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0;
             weights();
         }
         l_part += ls0 + ls1;
@@ -435,7 +439,10 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     TileCursor cur = c0;
     bool act_prev = false;
     bool act = n_tiles > 0 && wave_active(cur);
-    for (int t = 0;; ++t) {
+    // One step; kSt = t mod NS is a compile-time constant (the loop below runs
+    // NS steps per iteration), so every LDS stage offset is an immediate.
+    auto step = [&](int t, auto kst) {
+        constexpr int kSt = decltype(kst)::value;
         if (grp == 1) {
             if (t > 0) {
                 if (act_prev) softmax(cur);
@@ -443,12 +450,12 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
                 act = t < n_tiles && wave_active(cur);
             }
             __builtin_amdgcn_s_waitcnt(kWaitVm4);
-            load_tile(ld, t + 2 < n_tiles, (t + 2) & (NS - 1));
+            load_tile(ld, t + 2 < n_tiles, (kSt + 2) & (NS - 1));
             geo.advance(ld);
         }
         __builtin_amdgcn_s_setprio(1);
-        if (act_prev) compute_pv((t - 1) & (NS - 1));
-        if (act) compute_s(t & (NS - 1));
+        if (act_prev) compute_pv((kSt + NS - 1) & (NS - 1));
+        if (act) compute_s(kSt);
         __builtin_amdgcn_s_setprio(0);
         if (grp == 0) {
             if (t < n_tiles) {
@@ -457,15 +464,23 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
                 geo.advance(cur);
                 act = t + 1 < n_tiles && wave_active(cur);
                 __builtin_amdgcn_s_waitcnt(kWaitVm4);
-                load_tile(ld, t + 3 < n_tiles, (t + 3) & (NS - 1));
+                load_tile(ld, t + 3 < n_tiles, (kSt + 3) & (NS - 1));
                 geo.advance(ld);
             }
         } else {
             act_prev = act;
         }
-        if (t == n_tiles) break;
+        if (t == n_tiles) return true;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         bar();
+        return false;
+    };
+    static_assert(NS == 4, "the loop below runs one step per stage");
+    for (int t = 0;; t += NS) {
+        if (step(t, std::integral_constant<int, 0>{})) break;
+        if (step(t + 1, std::integral_constant<int, 1>{})) break;
+        if (step(t + 2, std::integral_constant<int, 2>{})) break;
+        if (step(t + 3, std::integral_constant<int, 3>{})) break;
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_waitcnt(0);   // no load may still be writing LDS when the workgroup ends
