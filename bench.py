@@ -60,15 +60,15 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # filled in from the counter summaries under profiles/ and valid only for the
 # kernel sources they were taken on.
 TRAFFIC = [
-    {"workload": "short", "order": "original",
-     "kernel_sources_sha256": "270e88977a1870ebf812f97bfa4f2c0789acebc6c1239fb999ab4d6af5a06b9e",
-     "bytes_per_launch": 161893422,
-     "fetch_bytes_per_launch": 124151245, "write_bytes_per_launch": 37742177,
-     "copy_scale": {"FETCH_SIZE": 1.99701, "WRITE_SIZE": 0.99992}},
     {"workload": "very_long", "order": "device",
-     "kernel_sources_sha256": "d957267665a42affdd6c6fe1bba01e5442b9573004ab3263322fd86f3b7f7d12",
-     "bytes_per_launch": 6177997644382,
-     "fetch_bytes_per_launch": 6170728382114, "write_bytes_per_launch": 7269262267,
+     "kernel_sources_sha256": "1d5b273412531a3b01eaf2097792d64229af7d59fd434afb0bff7caf592224a9",
+     "bytes_per_launch": 2468120784395,
+     "fetch_bytes_per_launch": 2460874814474, "write_bytes_per_launch": 7245969921,
+     "copy_scale": {"FETCH_SIZE": 1.99999, "WRITE_SIZE": 1.00000}},
+    {"workload": "very_long", "order": "original",
+     "kernel_sources_sha256": "1d5b273412531a3b01eaf2097792d64229af7d59fd434afb0bff7caf592224a9",
+     "bytes_per_launch": 6052105349089,
+     "fetch_bytes_per_launch": 6044919179706, "write_bytes_per_launch": 7186169383,
      "copy_scale": {"FETCH_SIZE": 1.99999, "WRITE_SIZE": 1.00000}},
 ]
 
