@@ -71,7 +71,8 @@ def build(jobs=None, extra=(), verbose=False):
         if verbose and err.strip():
             print(err, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an unresolved symbol fails the link instead of the first load.
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{p.stderr}")

@@ -108,11 +108,12 @@ struct __align__(16) SmemDq {
 // (round, 64-key tile) pairs, the rounds in source-device order (see
 // source() below). Per 32-key block: S^T = K Q^T
 // and dP^T = V dO^T on MFMA (Q^T and dO^T held in registers, K and V rows
-// from LDS), dS^T = P^T (dP^T - Delta) scale with P^T = 2^(S^T scale log2 e -
-// LSE log2 e), then dQ^T += K^T dS^T with K^T read transposed from the
-// row-major K tile through ds_read_b64_tr_b16. Waves 0-3 load K tiles and
-// waves 4-7 V tiles straight into a 4-stage LDS ring, three tiles ahead;
-// one barrier per tile.
+// from LDS), dS^T = P^T (dP^T - Delta) with P^T = 2^(S^T scale log2 e - LSE
+// log2 e), then dQ^T += K^T dS^T with K^T read transposed from the
+// row-major K tile through ds_read_b64_tr_b16; dQ takes the softmax scale
+// once at the end (one multiply per output instead of one per score). Waves
+// 0-3 load K tiles and waves 4-7 V tiles straight into a 4-stage LDS ring,
+// three tiles ahead; one barrier per tile.
 __global__ void __launch_bounds__(DQ_NT, 1) bwd_dq(BwdArgs a) {
     __shared__ SmemDq sm;
     const int L = (int)a.L;
@@ -300,7 +301,7 @@ __global__ void __launch_bounds__(DQ_NT, 1) bwd_dq(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sl, -lse_l2));
-                dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dlt) * scale);
+                dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dlt));
             }
 #pragma unroll
             for (int kk2 = 0; kk2 < 2; ++kk2)
@@ -322,8 +323,9 @@ __global__ void __launch_bounds__(DQ_NT, 1) bwd_dq(BwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const bf16x4 v4 = {(bf16)dqacc[db][4 * g], (bf16)dqacc[db][4 * g + 1], (bf16)dqacc[db][4 * g + 2],
-                               (bf16)dqacc[db][4 * g + 3]};
+            // dQ carries the softmax scale once here (its dS operands leave it out).
+            const bf16x4 v4 = {(bf16)(dqacc[db][4 * g] * scale), (bf16)(dqacc[db][4 * g + 1] * scale),
+                               (bf16)(dqacc[db][4 * g + 2] * scale), (bf16)(dqacc[db][4 * g + 3] * scale)};
             *(bf16x4*)(dqp + db * 32 + 8 * g + 4 * h2) = v4;
         }
 }
