@@ -336,3 +336,30 @@ def test_fwd_fused_small_dense_parity(sra, S, N, H):
         e_o, e_l = maxabs(np64(o), o_ref), maxabs(np64(lse), l_ref)
         assert e_o <= 2e-2 and e_l <= 2e-2, (layout, e_o, e_l)
         assert torch.equal(counts, _census(sra, S, N, layout, torch.bfloat16, H))
+
+
+@pytest.mark.parametrize("S,N,H", [(2048, 4, 2), (8 * 200, 8, 1)])
+def test_fwd_rising_scores_rescale(sra, S, N, H):
+    """Scores that rise along the sequence (keys grow along the queries' shared
+    direction, about 3 log2 units per 64-key tile): a row's running offset has
+    to be raised again and again within and across key tiles, so the weights'
+    overflow check, the exact row-max path and the pending O rescale all run.
+    Fused and per-round schedules, both layouts, against the dense fp64
+    oracle on the same bf16 inputs."""
+    g = torch.Generator().manual_seed(7 + S + N)
+    u = torch.randn(128, generator=g, dtype=torch.float64)
+    u /= u.norm()
+    ramp = (torch.arange(S, dtype=torch.float64) / S)[None, :, None, None]
+    q = 4.0 * u + 0.3 * torch.randn((1, S, H, 128), generator=g, dtype=torch.float64)
+    k = 200.0 * ramp * u + 0.3 * torch.randn((1, S, H, 128), generator=g, dtype=torch.float64)
+    v = 0.5 * torch.randn((1, S, H, 128), generator=g, dtype=torch.float64)
+    x = {n: t.to(torch.bfloat16) for n, t in (("q", q), ("k", k), ("v", v))}
+    o_ref, l_ref = oracle.dense_causal_attention(x["q"], x["k"], x["v"])
+    assert float(l_ref.max()) > 40.0   # the last rows' scores are far above their first ones
+    xg = {n: t.cuda() for n, t in x.items()}
+    for layout in LAYOUTS:
+        for name, run in (("fused", run_full_fused), ("per-round", run_full)):
+            o, lse, _ = run(sra, xg, N, layout)
+            e_o, e_l = maxabs(np64(o), o_ref), maxabs(np64(lse), l_ref)
+            say(f"rising scores S={S} N={N} layout={layout} {name}: O max-abs {e_o:.3g}  LSE {e_l:.3g}")
+            assert e_o <= 2e-2 and e_l <= 2e-2, (layout, name, e_o, e_l)
