@@ -31,7 +31,10 @@
 //  * Softmax runs in the log2 domain with v_exp_f32. The running offset is
 //    only raised when a tile's max exceeds it by more than 2^8 (the result
 //    does not depend on the offset; it only bounds p <= 256), so the
-//    64-register rescale of O is rare.
+//    64-register rescale of O is rare. The weights are taken against the
+//    current offset first and the row max is only computed when some
+//    lane's weights sum past 2^8 (which any weight past 2^8 implies), so
+//    the common step has no max at all.
 //  * K and V tiles go from HBM straight into a 4-stage LDS ring
 //    (buffer_load ... lds, no register staging), K three tiles and V two
 //    tiles ahead of the step that first reads them;
@@ -171,7 +174,8 @@ struct RoundGeom {
 // unit and the other on the vector ALU, and the two swap roles half-way; the
 // wave in X runs at raised issue priority. Group 0 loads K three tiles ahead
 // (in Y(t), K(t+3)), group 1 V two tiles ahead (at the start of its step,
-// V(t+2)).
+// V(t+2)). The loop body holds four steps, one per LDS stage, so that every
+// stage offset is a compile-time immediate.
 template <bool kFused>
 __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int flags) {
     __shared__ SmemBf16 sm;
