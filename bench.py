@@ -62,13 +62,13 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 TRAFFIC = [
     {"workload": "very_long", "order": "device",
      "kernel_sources_sha256": "f061a8a1578691c141787b3dc301c49446a1243046b7db06bf5c9fd3fa7cd6c6",
-     "bytes_per_launch": 2468120784395,
-     "fetch_bytes_per_launch": 2460874814474, "write_bytes_per_launch": 7245969921,
+     "bytes_per_launch": 2027301211163,
+     "fetch_bytes_per_launch": 2020054931994, "write_bytes_per_launch": 7246279168,
      "copy_scale": {"FETCH_SIZE": 1.99999, "WRITE_SIZE": 1.00000}},
     {"workload": "very_long", "order": "original",
      "kernel_sources_sha256": "f061a8a1578691c141787b3dc301c49446a1243046b7db06bf5c9fd3fa7cd6c6",
-     "bytes_per_launch": 6052105349089,
-     "fetch_bytes_per_launch": 6044919179706, "write_bytes_per_launch": 7186169383,
+     "bytes_per_launch": 5340605878429,
+     "fetch_bytes_per_launch": 5333423112820, "write_bytes_per_launch": 7182765609,
      "copy_scale": {"FETCH_SIZE": 1.99999, "WRITE_SIZE": 1.00000}},
 ]
 
