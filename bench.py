@@ -61,12 +61,12 @@ FWD_KERNEL_SOURCES = ("attn_fwd.hip", "kernel_common.h", "sra_internal.h")
 # kernel sources they were taken on.
 TRAFFIC = [
     {"workload": "very_long", "order": "device",
-     "kernel_sources_sha256": "f061a8a1578691c141787b3dc301c49446a1243046b7db06bf5c9fd3fa7cd6c6",
+     "kernel_sources_sha256": "951c1a8b95bee521cb70eb772cc448b5370a07eb045a792c7e4754302ce77b22",
      "bytes_per_launch": 2027301211163,
      "fetch_bytes_per_launch": 2020054931994, "write_bytes_per_launch": 7246279168,
      "copy_scale": {"FETCH_SIZE": 1.99999, "WRITE_SIZE": 1.00000}},
     {"workload": "very_long", "order": "original",
-     "kernel_sources_sha256": "f061a8a1578691c141787b3dc301c49446a1243046b7db06bf5c9fd3fa7cd6c6",
+     "kernel_sources_sha256": "951c1a8b95bee521cb70eb772cc448b5370a07eb045a792c7e4754302ce77b22",
      "bytes_per_launch": 5340605878429,
      "fetch_bytes_per_launch": 5333423112820, "write_bytes_per_launch": 7182765609,
      "copy_scale": {"FETCH_SIZE": 1.99999, "WRITE_SIZE": 1.00000}},

@@ -71,9 +71,9 @@ struct Decoded {
     int64_t b, h, d, s, qt, delta;
 };
 
-__device__ __forceinline__ Decoded decode_block(const RoundArgs& a, int64_t nqt) {
+__device__ __forceinline__ Decoded decode_block(const RoundArgs& a, int64_t nqt, bool group_major = false) {
     // Query tile heavy_rank 0 is the device's last (most live keys).
-    const WorkItem wi = decode_work(nqt, a.B, a.H, a.dev_hi - a.dev_lo, a.dev_lo);
+    const WorkItem wi = decode_work(nqt, a.B, a.H, a.dev_hi - a.dev_lo, a.dev_lo, group_major);
     Decoded o;
     o.b = wi.b;
     o.h = wi.h;
@@ -181,7 +181,12 @@ __global__ void __launch_bounds__(NT, 1) round_fwd_bf16_d128(RoundArgs a, int fl
     __shared__ SmemBf16 sm;
 
     const int64_t nqt = (a.L + BM - 1) / BM;
-    const Decoded blk = decode_block(a, nqt);
+    // One launch per round: every device of a head reads a different source
+    // slab, so with enough query tiles per device the workgroups go group by
+    // group (shared slab per XCD). With few tiles per device the interleaved
+    // heaviest-first order packs the CUs better. The all-rounds launch keeps
+    // the interleaved order: there all devices of a head read the same slab.
+    const Decoded blk = decode_block(a, nqt, !kFused && nqt >= 16);
     const int L = (int)a.L;   // the host bounds L * H * D so that in-slab offsets fit in 32 bits
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, c32 = lane & 31, h2 = lane >> 5;

@@ -140,11 +140,21 @@ __device__ __forceinline__ int clamp_delta(int64_t dl, int L) {
 struct WorkItem {
     int64_t b, h, d, heavy_rank;
 };
-__device__ __forceinline__ WorkItem decode_work(int64_t ntiles, int64_t B, int64_t H, int64_t nd, int64_t dev_lo) {
+__device__ __forceinline__ WorkItem decode_work(int64_t ntiles, int64_t B, int64_t H, int64_t nd, int64_t dev_lo,
+                                                bool group_major = false) {
     const int64_t G = B * H * nd;
     const int64_t i = blockIdx.x;
     int64_t qi, g;
-    if ((G & 7) == 0 && ((G >> 3) & 1) == 0) {
+    if (group_major && (G & 7) == 0) {
+        // One group at a time per XCD, its tiles heaviest first: the
+        // workgroups resident on an XCD then all read the one key/value slab
+        // of their group and share it through L2 (for launches whose groups
+        // read different slabs, such as one ring round of every device).
+        const int64_t gx = G >> 3;
+        const int64_t m = i >> 3;
+        qi = m % ntiles;
+        g = (i & 7) * gx + m / ntiles;
+    } else if ((G & 7) == 0 && ((G >> 3) & 1) == 0) {
         const int64_t gx = G >> 3, hx = gx >> 1;
         const int64_t m = i >> 3;
         const int64_t half = hx * ntiles;
