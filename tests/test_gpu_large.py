@@ -105,7 +105,7 @@ def _unit_rows(w, seed):
     return u / u.norm(dim=-1, keepdim=True)
 
 
-@pytest.mark.parametrize("layout,schedule", [(oracle.STRIPED, 1), (oracle.CONTIGUOUS, 0)])
+@pytest.mark.parametrize("layout,schedule", [(oracle.STRIPED, 1), (oracle.STRIPED, 0), (oracle.CONTIGUOUS, 0)])
 def test_long_forward_previous_match_all_rows(sra, long_inputs, layout, schedule):
     """Q_i = c * U_(i-1), K = c * U (row 0 matches itself): the previous key
     scores 64 and dominates, so O_i = V_(i-1) on every row and head -- the key
@@ -118,7 +118,7 @@ def test_long_forward_previous_match_all_rows(sra, long_inputs, layout, schedule
     o, lse = forward(sra, q, k, v, w["n_dev"], layout, schedule)
     want = torch.cat([v[:, :1], v[:, :-1]], dim=1)
     err = (o.float() - want.float()).abs().max().item()
-    say(f"long previous-match layout={layout}: max |O_i - V_(i-1)| {err:.3g}")
+    say(f"long previous-match layout={layout} schedule={schedule}: max |O_i - V_(i-1)| {err:.3g}")
     assert err <= 2e-2
 
 
@@ -147,11 +147,12 @@ def very_long():
 
 @pytest.fixture(scope="module")
 def very_long_bench_fwd(sra, very_long):
-    """The forward launch the benchmark times at Very long: striped, fused
-    schedule, tensors in original token order (each device's stripe read in
-    place), 786,432 tokens on 16 devices."""
+    """The fused striped forward at Very long (786,432 tokens on 16 devices)
+    with tensors in original token order (each device's stripe read in
+    place). The benchmark times the same launch on the device-layout copies
+    (test_very_long_device_order_bit_identical ties the two together)."""
     w, x = very_long
-    say("very long: fused original-order forward (the benchmark's launch) ...")
+    say("very long: fused original-order forward ...")
     o, lse = sra.ring_attn_fwd(x["q"], x["k"], x["v"], w["n_dev"], oracle.STRIPED, schedule=sra.SCHEDULE_FUSED,
                                order=sra.ORDER_ORIGINAL)
     torch.cuda.synchronize()
@@ -294,3 +295,52 @@ def test_very_long_zero_query_closed_forms(sra, very_long):
     e_dv = float(np.abs(np64(dv[:, :, heads]) - dv_ref).max())
     say(f"very long Q=0: LSE {e_l:.3g}  dK exactly 0  dV {e_dv:.3g}")
     assert e_l <= 2e-2 and e_dv <= 2e-2
+
+
+def test_very_long_device_order_bit_identical(sra, very_long, very_long_bench_fwd):
+    """The benchmark's Very long step: stripe-permute Q, K, V (and dO) into the
+    device layout, the fused forward and the backward on those copies, then
+    unstripe. Its outputs must equal the original-order launches' bit for bit
+    (the same kernels, reading the same rows at other addresses), so the
+    parity tests of the original-order launches cover it."""
+    w, x = very_long
+    o, lse = very_long_bench_fwd
+    N = w["n_dev"]
+    qd, kd, vd = (sra.stripe_permute(x[n], N) for n in ("q", "k", "v"))
+    say("very long: fused forward in device order ...")
+    od, ld = sra.ring_attn_fwd(qd, kd, vd, N, oracle.STRIPED, schedule=sra.SCHEDULE_FUSED)
+    torch.cuda.synchronize()
+    assert torch.equal(sra.unstripe(od, N), o) and torch.equal(sra.unstripe(ld, N), lse)
+    say("very long: device-order forward bit-identical; backward in both orders ...")
+    dod = sra.stripe_permute(x["do"], N)
+    g_dev = sra.ring_attn_bwd(qd, kd, vd, od, ld, dod, N, oracle.STRIPED)
+    del qd, kd, vd, od, ld, dod
+    g_dev = [sra.unstripe(t, N) for t in g_dev]
+    g_org = sra.ring_attn_bwd(x["q"], x["k"], x["v"], o, lse, x["do"], N, oracle.STRIPED, order=sra.ORDER_ORIGINAL)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), g_dev, g_org):
+        assert torch.equal(a, b), name
+    say("very long: device-order backward bit-identical")
+
+
+def test_very_long_per_round_previous_match_all_rows(sra, very_long):
+    """Q_i = c * U_(i-1): O_i = V_(i-1) on every row and head at N = 16 through
+    the one-launch-per-ring-round schedule on device-layout tensors (the
+    benchmark's per-round comparison launch; each round's launch takes the
+    groups of (batch, head, device) one at a time per XCD at this size)."""
+    w, x = very_long
+    N = w["n_dev"]
+    c = math.sqrt(64.0 * math.sqrt(w["head_dim"]))
+    k = (c * _unit_rows(w, 46)).to(torch.bfloat16)
+    q = torch.cat([k[:, :1], k[:, :-1]], dim=1).contiguous()
+    qd, kd = sra.stripe_permute(q, N), sra.stripe_permute(k, N)
+    del q, k
+    vd = sra.stripe_permute(x["v"], N)
+    od, _ = sra.ring_attn_fwd(qd, kd, vd, N, oracle.STRIPED, schedule=sra.SCHEDULE_PER_ROUND)
+    del qd, kd, vd
+    o = sra.unstripe(od, N)
+    torch.cuda.synchronize()
+    want = torch.cat([x["v"][:, :1], x["v"][:, :-1]], dim=1)
+    err = (o.float() - want.float()).abs().max().item()
+    say(f"very long per-round previous-match: max |O_i - V_(i-1)| {err:.3g}")
+    assert err <= 2e-2
