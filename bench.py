@@ -625,6 +625,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        # Step throughput over the oracle's (extrapolated) rate on the host cores.
+        rec["cpu_baseline"]["gpu_over_cpu"] = value / rec["cpu_baseline"]["value"]
         note("cpu baseline done")
     print(json.dumps(rec), flush=True)
 
