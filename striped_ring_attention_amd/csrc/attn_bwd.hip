@@ -60,27 +60,40 @@ constexpr int D = 128;
 // Row statistics of the backward, one float pair per row in a head-major
 // layout [B, H, S, 2]: (LSE * log2 e, Delta), Delta = sum_c dO[c] * O[c] in
 // fp32. The rows of one head are contiguous, so the 32 rows of a query tile
-// are 256 contiguous bytes. Sixteen lanes per (b, slot, h) row, each taking
-// 8 consecutive elements (16-byte loads: a wave reads four whole 256-byte
-// rows of O and of dO), then a 16-lane butterfly sum.
+// are 256 contiguous bytes. A workgroup takes 16 slots x up to 64 heads of one
+// batch: sixteen lanes per (b, slot, h) row, each taking 8 consecutive
+// elements (16-byte loads; consecutive rows of a pass are consecutive heads
+// of one slot, so a wave reads four whole 256-byte rows of O and of dO), a
+// 16-lane butterfly sum, and the pair parked in LDS as [head][slot]. The
+// pairs then go out head by head, 16 slots = 128 contiguous bytes, instead of
+// one 8-byte store per row across the head-major array.
+constexpr int kDeltaSlots = 16;
+constexpr int kDeltaHeads = 64;
 __global__ void __launch_bounds__(256) bwd_delta(const bf16* __restrict__ o, const bf16* __restrict__ dout,
                                                  const float* __restrict__ lse, float* __restrict__ stats,
-                                                 uint32_t rows, uint32_t S, uint32_t H) {
-    const uint32_t stride = (gridDim.x * blockDim.x) >> 4;
+                                                 uint32_t S, uint32_t H) {
+    __shared__ float2 tile[kDeltaHeads][kDeltaSlots];
+    const uint32_t n_sb = (S + kDeltaSlots - 1) / kDeltaSlots, n_hb = (H + kDeltaHeads - 1) / kDeltaHeads;
+    const uint32_t hb = blockIdx.x % n_hb, sb = (blockIdx.x / n_hb) % n_sb, b = blockIdx.x / n_hb / n_sb;
+    const uint32_t s0 = sb * kDeltaSlots, h0 = hb * kDeltaHeads;
+    const uint32_t ns = min((uint32_t)kDeltaSlots, S - s0), nh = min((uint32_t)kDeltaHeads, H - h0);
     const int c = threadIdx.x & 15;
-    for (uint32_t r = (blockIdx.x * blockDim.x + threadIdx.x) >> 4; r < rows; r += stride) {
-        const bf16x8 x = *(const bf16x8*)(o + (uint64_t)r * D + 8 * c);
-        const bf16x8 y = *(const bf16x8*)(dout + (uint64_t)r * D + 8 * c);
-        float s = 0.f;
+    for (uint32_t i = threadIdx.x >> 4; i < ns * nh; i += 16) {
+        const uint32_t si = i / nh, hk = i - si * nh;
+        const uint64_t r = ((uint64_t)b * S + s0 + si) * H + h0 + hk;
+        const bf16x8 x = *(const bf16x8*)(o + r * D + 8 * c);
+        const bf16x8 y = *(const bf16x8*)(dout + r * D + 8 * c);
+        float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
+        for (int e = 0; e < 8; ++e) sum = __builtin_fmaf((float)x[e], (float)y[e], sum);
 #pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
-        if (c == 0) {
-            const uint32_t h = r % H, bs = r / H, b = bs / S, slot = bs % S;
-            const uint64_t i = ((uint64_t)b * H + h) * S + slot;
-            *(float2*)(stats + 2 * i) = float2{lse[r] * kLog2e, s};
-        }
+        for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 16);
+        if (c == 0) tile[hk][si] = float2{lse[r] * kLog2e, sum};
+    }
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < nh * kDeltaSlots; i += 256) {
+        const uint32_t hk = i / kDeltaSlots, si = i % kDeltaSlots;
+        if (si < ns) *(float2*)(stats + 2 * (((uint64_t)b * H + h0 + hk) * S + s0 + si)) = tile[hk][si];
     }
 }
 
@@ -358,12 +371,11 @@ hipError_t bwd_scratch(void** ptr) {
 hipError_t launch_bwd_dkdv_bf16_d128(const BwdArgs& a, hipStream_t stream);
 
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, hipStream_t stream) {
-    const uint64_t rows = (uint64_t)(a.B * a.S * a.H);
-    uint64_t blocks = (rows + 15) / 16;   // 16 rows per 256-thread block
-    if (blocks > 256ull * 64) blocks = 256ull * 64;
+    const uint64_t blocks = (uint64_t)a.B * ((a.S + kDeltaSlots - 1) / kDeltaSlots) *
+                            ((a.H + kDeltaHeads - 1) / kDeltaHeads);
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(bwd_delta, dim3((unsigned)blocks), dim3(256), 0, stream, (const bf16*)a.o, (const bf16*)a.dout,
-                       a.lse, a.stats, (uint32_t)rows, (uint32_t)a.S, (uint32_t)a.H);
+                       a.lse, a.stats, (uint32_t)a.S, (uint32_t)a.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nq = (a.L + QBM - 1) / QBM * a.H * a.N * a.B;
