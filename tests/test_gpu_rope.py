@@ -123,3 +123,21 @@ def test_striped_attention_over_rotated_inputs(sra, order):
     e_l = float(np.abs(lse.double().cpu().numpy() - l_ref).max())
     say(f"attention over rotated inputs ({order}): O {e_o:.3g} LSE {e_l:.3g}")
     assert e_o <= 2e-2 and e_l <= 2e-2
+
+
+def test_rope_large_striped(sra):
+    """A striped tensor of 512 MB (the Long workload's Q at 8 heads):
+    unstriped, its output equals the original-order call bit for bit, with and
+    without explicit position ids, and sampled rows match the oracle."""
+    B, S, H, D, N = 1, 262144, 8, 128, 8
+    x = rand((B, S, H, D), torch.bfloat16, 9)
+    g = torch.Generator(device="cuda").manual_seed(10)
+    for pos in (None, torch.randint(0, 1_000_000, (B, S), generator=g, device="cuda", dtype=torch.int64)):
+        y = sra.rope_permute(x, N, oracle.STRIPED, pos=pos)
+        y2 = sra.rope_permute(x, N, oracle.STRIPED, pos=pos, order=sra.ORDER_ORIGINAL)
+        torch.cuda.synchronize()
+        assert torch.equal(sra.unstripe(y, N), y2)
+        rows = np.unique(np.concatenate([[0, 1, N, S - 1], np.random.default_rng(11).integers(0, S, 60)]))
+        p = rows[None, :] if pos is None else pos[:, rows].cpu().numpy()
+        e = check_close(y2[:, rows], oracle.rope(x[:, rows].cpu(), p), torch.bfloat16)
+        say(f"large striped rope pos={'ids' if pos is not None else 'index'}: sampled rows {e:.3g}, bit-identical orders")
