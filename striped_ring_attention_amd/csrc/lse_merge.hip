@@ -69,8 +69,12 @@ hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_part, c
     while ((1u << shift) < q) ++shift;
     uint64_t total = (uint64_t)rows * q;
     const int threads = 256;
+    // One chunk per thread (the loop covers grids past the launch limit): with
+    // every chunk its own thread the loads of many waves are in flight. A grid
+    // capped at 16,384 workgroups, each thread looping over ~200 chunks, moved
+    // 5.1 TB/s at 25 M rows; this grid moves 6.56 TB/s (6.47 at 2.1 M rows).
     uint64_t blocks = (total + threads - 1) / threads;
-    if (blocks > 256ull * 64) blocks = 256ull * 64;
+    if (blocks > 0x7fffffffull) blocks = 0x7fffffffull;
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, (f32x4*)o_acc, lse_acc,
                        (const f32x4*)o_part, lse_part, (uint64_t)rows, q, shift);
