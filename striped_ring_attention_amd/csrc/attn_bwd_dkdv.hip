@@ -132,33 +132,58 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     const uint32_t lds_st = lds_addr(&sm.st[0][w][0]);
     constexpr uint32_t kTileBytes = KBQ * D * 2;
     constexpr uint32_t kStBytes = 8 * 64 * 4;
-    // Loader cursor (round lr, query tile lq) and, for its tile, the byte
-    // offset of the first row from the head's base, the bytes from there to
-    // the end of the device's slab, and the first row's statistics slot.
+    // Loader cursor (round lr, query tile lq) and, for its tile, the
+    // addresses of its first Q and dO rows and of its first statistics slot,
+    // and the statistics bytes left from there to the end of the head. Every
+    // round's slab has L rows, so only a round's last tile can be partial:
+    // its Q/dO loads may read kLastRec bytes (rows past the slab read as
+    // zero), every other tile's kFullRec. Per tile the loader only adds
+    // strides; the round change happens apart from the loads (ld_settle).
+    const int kFullRec = KBQ * rstride;
+    const int kLastRec = (int)(span_bytes - (int64_t)(nqt - 1) * KBQ * rstride);
+    const int kStFull = KBQ * rstep * 8;
     int lr = 0, lq = first_tile(0);
     settle(lr, lq);
-    int64_t ld_off = 0, ld_left = 0, st_row = 0;
+    uint64_t ld_q = 0, ld_do = 0, ld_st = 0;
+    int st_left = 0;
     auto ld_enter = [&]() {
         const int dq = qdev(lr);
-        ld_off = mem_slot(strided, N, a.L, dq, 0) * (int64_t)row_bytes + (int64_t)lq * KBQ * rstride;
-        ld_left = span_bytes - (int64_t)lq * KBQ * rstride;
-        st_row = mem_slot(strided, N, a.L, dq, (int64_t)lq * KBQ);
+        const int64_t off = mem_slot(strided, N, a.L, dq, 0) * (int64_t)row_bytes + (int64_t)lq * KBQ * rstride;
+        const int64_t st_row = mem_slot(strided, N, a.L, dq, (int64_t)lq * KBQ);
+        ld_q = uniform_u64(q_head + (uint64_t)off);
+        ld_do = uniform_u64(do_head + (uint64_t)off);
+        ld_st = uniform_u64(st_head + (uint64_t)st_row * 8);
+        st_left = __builtin_amdgcn_readfirstlane((int)min((a.S - st_row) * 8, (int64_t)0x7FFFFFFF));
     };
     ld_enter();
-    auto load_tile = [&](bool valid, int stage) {
-        const int left = (valid && ld_left > 0) ? (int)min(ld_left, (int64_t)KBQ * rstride) : 0;
-        const int st_left = valid ? (int)min((a.S - st_row) * 8, (int64_t)KBQ * rstep * 8) : 0;
-        const i32x4 rq = raw_rsrc(q_head + (uint64_t)ld_off, left);
-        const i32x4 rd = raw_rsrc(do_head + (uint64_t)ld_off, left);
-        const i32x4 rst = raw_rsrc(st_head + (uint64_t)st_row * 8, st_left);
-        load_lds_b128(rq, ld_voff, lds_q + stage * kTileBytes);
-        load_lds_b128(rd, ld_voff, lds_do + stage * kTileBytes);
-        load_lds_b32(rst, st_voff, lds_st + stage * kStBytes);
-        ++lq;
-        ld_off += (int64_t)KBQ * rstride;
-        ld_left -= (int64_t)KBQ * rstride;
-        st_row += (int64_t)KBQ * rstep;
+    auto ld_settle = [&]() {
         if (settle(lr, lq)) ld_enter();
+    };
+    // The three loads of the loader's tile (all reading zero when !valid),
+    // then the cursor moved to the next tile of the round.
+    auto load_q = [&](bool valid, int stage) {
+        const int rec = valid ? (lq == nqt - 1 ? kLastRec : kFullRec) : 0;
+        load_lds_b128(raw_rsrc(ld_q, rec), ld_voff, lds_q + stage * kTileBytes);
+    };
+    auto load_do = [&](bool valid, int stage) {
+        const int rec = valid ? (lq == nqt - 1 ? kLastRec : kFullRec) : 0;
+        load_lds_b128(raw_rsrc(ld_do, rec), ld_voff, lds_do + stage * kTileBytes);
+    };
+    auto load_st = [&](bool valid, int stage) {
+        load_lds_b32(raw_rsrc(ld_st, valid ? min(st_left, kStFull) : 0), st_voff, lds_st + stage * kStBytes);
+    };
+    auto ld_advance = [&]() {
+        ++lq;
+        ld_q += (uint64_t)kFullRec;
+        ld_do += (uint64_t)kFullRec;
+        ld_st += (uint64_t)kStFull;
+        st_left -= kStFull;
+    };
+    auto load_tile = [&](bool valid, int stage) {
+        load_q(valid, stage);
+        load_do(valid, stage);
+        load_st(valid, stage);
+        ld_advance();
     };
 
     // Transposing-read addressing (lane (g, j) names query row 16 kk2 + 8 rd +
@@ -183,7 +208,10 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
         bar();
     }
 #pragma unroll 1
-    for (int u = 0; u < DK_AHEAD; ++u) load_tile(u < n_tiles, u);
+    for (int u = 0; u < DK_AHEAD; ++u) {
+        load_tile(u < n_tiles, u);
+        ld_settle();
+    }
     __builtin_amdgcn_s_waitcnt(0);   // the K/V operands and tiles 0..4 are in
     bar();
 
@@ -242,36 +270,58 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     // each wave's step.)
     int cr = 0, cq = first_tile(0);
     settle(cr, cq);
-    int c_delta = delta_of(cr);
+    // Per round of the compute cursor: the group has live pairs in tile cq
+    // iff its first key is live for the tile's last row, i.e. iff
+    // cq >= c_act; the tile is fully live for the group (every row in range
+    // and the group's last key live for the tile's first row) iff
+    // c_full_lo <= cq < c_full_hi.
+    constexpr int kNever = 1 << 30;
+    int c_delta = 0, c_act = kNever, c_full_lo = kNever;
+    const int c_full_hi = kw0 + 31 < L ? L / KBQ : 0;
+    auto c_enter = [&]() {
+        c_delta = delta_of(cr);
+        const int need = kw0 - c_delta + 1;   // the tile's last row must be at least this
+        c_act = __builtin_amdgcn_readfirstlane(wave_live && need <= L - 1 ? max(need, 0) / KBQ : kNever);
+        const int m = kw0 + 31 - c_delta;     // the tile's first row must exceed this
+        c_full_lo = __builtin_amdgcn_readfirstlane(m < 0 ? 0 : m / KBQ + 1);
+    };
+    c_enter();
     int stg = 0, stg_prev = 0, stg_ld = DK_AHEAD;
     bool act_prev = false;
     f32x16 x;        // S of tile t (P wave) or dP of tile t-1 (dS wave)
     bf16x8 opb[2];   // P of tile t-1 (P wave) or dS of tile t-1 (dS wave), bf16 MFMA operand
-    auto step_begin = [&](int t) {
-        load_tile(t + DK_AHEAD < n_tiles, stg_ld);   // into the stage of tile t-2
-        stg_ld = next_stage(stg_ld);
-        const int jq0 = cq * KBQ;
-        const int jq_last = min(jq0 + KBQ - 1, L - 1);
-        // Live pairs for this group: its first key is live for the tile's last row.
-        return t < n_tiles && wave_live && kw0 < live32(jq_last, c_delta, L);
-    };
     auto step_end = [&](int t, bool act) {
         if (t < n_tiles) {
             ++cq;
-            if (settle(cr, cq)) c_delta = delta_of(cr);
+            if (settle(cr, cq)) c_enter();
         }
         act_prev = act;
         stg_prev = stg;
         stg = next_stage(stg);
+        stg_ld = next_stage(stg_ld);
+        ld_settle();
         __builtin_amdgcn_s_waitcnt(kWaitVm12);   // tile t+1 is in
     };
 
     if (!ds_wave) {
-        bf16x8 yt[2][4];   // dO^T of tile t-1
+        // dO^T of tile t-1 and P of tile t-1: the dV product runs every step,
+        // on zero P when that tile had no work for the group (adding zero
+        // products leaves dV as it is), so both start at zero.
+        bf16x8 yt[2][4];
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+            opb[kk2] = bf16x8{};
+#pragma unroll
+            for (int db = 0; db < 4; ++db) yt[kk2][db] = bf16x8{};
+        }
         for (int t = 0; t <= n_tiles; ++t) {
-            const bool act = step_begin(t);
+            const bool act = t < n_tiles && cq >= c_act;
+            const bool ld_valid = t + DK_AHEAD < n_tiles;
             const int jq0 = cq * KBQ;
-            // Phase A: dV^T += dO^T P (tile t-1), S of tile t.
+            // Phase A: Q rows and LSE of tile t read; dV^T += dO^T P (tile
+            // t-1) with the step's three tile loads (into the stage of tile
+            // t-2) and the loader's advance issued between its MFMAs; S of
+            // tile t.
             bf16x8 xr[8];
             f32x4 lz[4];   // LSE log2 e of rows 8g + 4h2 .. +3
             read_rows(sm.q[stg], xr);
@@ -281,16 +331,24 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
                 for (int g = 0; g < 4; ++g) lz[g] = *(const f32x4*)&stt[8 * g + 4 * h2];
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (act_prev) acc_t(yt, opb);
+#pragma unroll
+            for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yt[kk2][db], opb[kk2], acc[db], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (kk2 == 0 && db == 0) load_q(ld_valid, stg_ld);
+                    if (kk2 == 0 && db == 1) load_do(ld_valid, stg_ld);
+                    if (kk2 == 0 && db == 2) load_st(ld_valid, stg_ld);
+                    if (kk2 == 0 && db == 3) ld_advance();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             if (act) x = rows_kv(xr);
             // Phase B: P of tile t, written for the dS wave; dO^T of tile t read.
             read_yt(sm.dout[stg], yt);
             __builtin_amdgcn_sched_barrier(0);
             if (act) {
-                // The tile is fully live when all its rows are in range and
-                // the group's last key is live for the tile's first row.
-                const bool full = jq0 + KBQ <= L && kw0 + 31 < L && kw0 + 31 < jq0 + c_delta;
-                if (!full) {
+                if (!(cq >= c_full_lo && cq < c_full_hi)) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int jj = jq0 + 8 * (i >> 2) + 4 * h2 + (i & 3);
@@ -308,6 +366,9 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
                     }
                     pex(t)[64 * g] = pq;
                 }
+            } else {
+                opb[0] = bf16x8{};
+                opb[1] = bf16x8{};
             }
             step_end(t, act);
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // P is in LDS
@@ -315,7 +376,8 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
         }
     } else {
         for (int t = 0; t <= n_tiles; ++t) {
-            const bool act = step_begin(t);
+            load_tile(t + DK_AHEAD < n_tiles, stg_ld);   // into the stage of tile t-2
+            const bool act = t < n_tiles && cq >= c_act;
             // Phase A: dS of tile t-1 from P, dP and Delta; dO rows of tile t read.
             f32x4 pq[4], dz[4];
             bf16x8 xr[8];
