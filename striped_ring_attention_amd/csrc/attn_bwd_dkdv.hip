@@ -133,19 +133,20 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     constexpr uint32_t kTileBytes = KBQ * D * 2;
     constexpr uint32_t kStBytes = 8 * 64 * 4;
     // Loader cursor (round lr, query tile lq) and, for its tile, the
-    // addresses of its first Q and dO rows and of its first statistics slot,
-    // and the statistics bytes left from there to the end of the head. Every
-    // round's slab has L rows, so only a round's last tile can be partial:
-    // its Q/dO loads may read kLastRec bytes (rows past the slab read as
-    // zero), every other tile's kFullRec. Per tile the loader only adds
-    // strides; the round change happens apart from the loads (ld_settle).
+    // addresses of its first Q and dO rows and of its first statistics slot.
+    // Every round's slab has L rows, so only a round's last tile can be
+    // partial: its Q/dO loads may read kLastRec bytes (rows past the slab
+    // read as zero) and its statistics load st_last bytes (up to the end of
+    // the head's statistics), every other tile kFullRec and kStFull. Per tile
+    // the loader only adds strides; the round change happens apart from the
+    // loads (ld_settle).
     const int kFullRec = KBQ * rstride;
     const int kLastRec = (int)(span_bytes - (int64_t)(nqt - 1) * KBQ * rstride);
     const int kStFull = KBQ * rstep * 8;
     int lr = 0, lq = first_tile(0);
     settle(lr, lq);
     uint64_t ld_q = 0, ld_do = 0, ld_st = 0;
-    int st_left = 0;
+    int st_last = 0;
     auto ld_enter = [&]() {
         const int dq = qdev(lr);
         const int64_t off = mem_slot(strided, N, a.L, dq, 0) * (int64_t)row_bytes + (int64_t)lq * KBQ * rstride;
@@ -153,7 +154,8 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
         ld_q = uniform_u64(q_head + (uint64_t)off);
         ld_do = uniform_u64(do_head + (uint64_t)off);
         ld_st = uniform_u64(st_head + (uint64_t)st_row * 8);
-        st_left = __builtin_amdgcn_readfirstlane((int)min((a.S - st_row) * 8, (int64_t)0x7FFFFFFF));
+        const int64_t st_row_last = mem_slot(strided, N, a.L, dq, (int64_t)(nqt - 1) * KBQ);
+        st_last = __builtin_amdgcn_readfirstlane((int)min((a.S - st_row_last) * 8, (int64_t)kStFull));
     };
     ld_enter();
     auto ld_settle = [&]() {
@@ -170,14 +172,14 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
         load_lds_b128(raw_rsrc(ld_do, rec), ld_voff, lds_do + stage * kTileBytes);
     };
     auto load_st = [&](bool valid, int stage) {
-        load_lds_b32(raw_rsrc(ld_st, valid ? min(st_left, kStFull) : 0), st_voff, lds_st + stage * kStBytes);
+        const int rec = valid ? (lq == nqt - 1 ? st_last : kStFull) : 0;
+        load_lds_b32(raw_rsrc(ld_st, rec), st_voff, lds_st + stage * kStBytes);
     };
     auto ld_advance = [&]() {
         ++lq;
         ld_q += (uint64_t)kFullRec;
         ld_do += (uint64_t)kFullRec;
         ld_st += (uint64_t)kStFull;
-        st_left -= kStFull;
     };
     auto load_tile = [&](bool valid, int stage) {
         load_q(valid, stage);
