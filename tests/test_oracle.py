@@ -616,3 +616,40 @@ def test_planted_mistake_is_caught(case):
     pin(oracle)                         # the real oracle passes the pin ...
     with pytest.raises(AssertionError):
         pin(mod)                        # ... the mutant fails it
+
+
+# ------------------------------------------------- generated shapes (hypothesis) --
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(n_dev=st.integers(1, 6), L=st.integers(1, 5), D=st.integers(1, 4),
+       layout=st.sampled_from([ost.CONTIGUOUS, ost.STRIPED]), seed=st.integers(0, 2**16),
+       pick=st.integers(0, 35))
+def test_generated_shapes_ring_matches_brute_force(n_dev, L, D, layout, seed, pick):
+    """On generated shapes: the ring over all rounds, taken back to original
+    order, equals causal attention by pure-Python loops; and one generated
+    (device, round) partial equals the brute-force masked softmax over the
+    keys whose position (the layout's wording) is at most the query's."""
+    S = n_dev * L
+    q, k, v = (rand((1, S, 1, D), seed + i) for i in range(3))
+    scale = 1.0 / math.sqrt(D)
+    O, LSE = bf_causal(q[0, :, 0].tolist(), k[0, :, 0].tolist(), v[0, :, 0].tolist(), scale)
+    dev = [oracle.to_device_layout(t, n_dev, layout) for t in (q, k, v)]
+    o, lse = oracle.ring_attention(*dev, n_dev, layout)
+    o, lse = oracle.from_device_layout(o, n_dev, layout), oracle.from_device_layout(lse, n_dev, layout)
+    np.testing.assert_allclose(o[0, :, 0], np.array(O), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, :, 0], np.array(LSE), rtol=0, atol=1e-12)
+
+    d, r = pick % n_dev, (pick // n_dev) % n_dev
+    src = (d - r) % n_dev
+    op, lp = oracle.ring_partial(*dev, n_dev, layout, d, r)
+    live = [[explicit_position(n_dev, L, layout, src, kk) <= explicit_position(n_dev, L, layout, d, j)
+             for kk in range(L)] for j in range(L)]
+    Op, Lp = bf_masked(dev[0][0, d * L:(d + 1) * L, 0].tolist(), dev[1][0, src * L:(src + 1) * L, 0].tolist(),
+                       dev[2][0, src * L:(src + 1) * L, 0].tolist(), live, scale)
+    np.testing.assert_allclose(op[0, :, 0], np.array(Op), rtol=0, atol=1e-12)
+    assert np.array_equal(np.isneginf(lp[0, :, 0]), np.isneginf(np.array(Lp)))
+    fin = np.isfinite(np.array(Lp))
+    np.testing.assert_allclose(lp[0, fin, 0], np.array(Lp)[fin], rtol=0, atol=1e-12)
