@@ -15,7 +15,9 @@ constexpr int KBQ = 32;           // query rows per tile
 constexpr int DK_NT = 512;        // 8 waves: two per key group
 constexpr int DK_NS = 7;          // LDS stages
 constexpr int DK_AHEAD = 5;       // tiles in flight ahead of the one computed
-constexpr int kWaitVm12 = 0x0F7C; // vmcnt(12): the four newest tiles (3 loads each per wave) may be in flight
+constexpr int kWaitVm12 = 0x0F7C; // vmcnt(12): the four newest tiles (3 loads each, the statistics wave) may be in flight
+constexpr int kWaitVm8 = 0x0F78;  // vmcnt(8): the same for the other waves (2 loads each)
+constexpr int kStWave = 4;        // the wave that loads each tile's row statistics
 
 // Q and dO tiles are stored row-major with 256-byte rows and no padding
 // (they are loaded straight into LDS); 16-byte chunk c of row r sits in slot
@@ -28,7 +30,7 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 struct __align__(16) SmemDkdv {
     bf16 q[DK_NS][KBQ * D];       // Q tiles
     bf16 dout[DK_NS][KBQ * D];    // dO tiles
-    float st[DK_NS][8][64];       // per wave: LSE log2 e of the tile's 32 rows, then their Delta
+    float st[DK_NS][64];          // LSE log2 e of the tile's 32 rows, then their Delta
     f32x4 p[2][4][4][64];         // P of tiles t (slot t % 2) and t-1: [slot][group][register quad][lane]
 };
 
@@ -123,15 +125,17 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     // Loads: wave w issues instruction w of each 8-instruction (8 KiB) tile of
     // Q and of dO, covering rows 4w .. 4w+3: lane l writes row 4w + l/16,
     // slot l % 16, loading the chunk that slot holds (for these rows
-    // swz = 4 (l/16) + w % 4). Each wave also loads the tile's statistics into
-    // its own copy: lane l takes row l % 32, LSE for l < 32 and Delta above.
+    // swz = 4 (l/16) + w % 4). Wave kStWave also loads the tile's statistics
+    // into the one copy every wave reads: lane l takes row l % 32, LSE for
+    // l < 32 and Delta above. Each wave waits for its own loads of a tile
+    // before the barrier that precedes the tile's first read.
     const int ld_voff = (4 * w + (lane >> 4)) * rstride + 16 * ((lane & 15) ^ (((lane >> 4) << 2) | kg));
     const int st_voff = (lane & 31) * rstep * 8 + (lane >> 5) * 4;
     const uint32_t lds_q = lds_addr(&sm.q[0][0]) + 1024 * w;
     const uint32_t lds_do = lds_addr(&sm.dout[0][0]) + 1024 * w;
-    const uint32_t lds_st = lds_addr(&sm.st[0][w][0]);
+    const uint32_t lds_st = lds_addr(&sm.st[0][0]);
     constexpr uint32_t kTileBytes = KBQ * D * 2;
-    constexpr uint32_t kStBytes = 8 * 64 * 4;
+    constexpr uint32_t kStBytes = 64 * 4;
     // Loader cursor (round lr, query tile lq) and, for its tile, the
     // addresses of its first Q and dO rows and of its first statistics slot.
     // Every round's slab has L rows, so only a round's last tile can be
@@ -173,7 +177,7 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
     };
     auto load_st = [&](bool valid, int stage) {
         const int rec = valid ? (lq == nqt - 1 ? st_last : kStFull) : 0;
-        load_lds_b32(raw_rsrc(ld_st, rec), st_voff, lds_st + stage * kStBytes);
+        if (w == kStWave) load_lds_b32(raw_rsrc(ld_st, rec), st_voff, lds_st + stage * kStBytes);
     };
     auto ld_advance = [&]() {
         ++lq;
@@ -302,7 +306,10 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
         stg = next_stage(stg);
         stg_ld = next_stage(stg_ld);
         ld_settle();
-        __builtin_amdgcn_s_waitcnt(kWaitVm12);   // tile t+1 is in
+        if (w == kStWave)   // tile t+1 is in
+            __builtin_amdgcn_s_waitcnt(kWaitVm12);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitVm8);
     };
 
     if (!ds_wave) {
@@ -328,7 +335,7 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
             f32x4 lz[4];   // LSE log2 e of rows 8g + 4h2 .. +3
             read_rows(sm.q[stg], xr);
             {
-                const float* stt = sm.st[stg][w];
+                const float* stt = sm.st[stg];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) lz[g] = *(const f32x4*)&stt[8 * g + 4 * h2];
             }
@@ -384,7 +391,7 @@ __global__ void __launch_bounds__(DK_NT, 1) bwd_dkdv(BwdArgs a) {
             f32x4 pq[4], dz[4];
             bf16x8 xr[8];
             {
-                const float* stp = sm.st[stg_prev][w];
+                const float* stp = sm.st[stg_prev];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     pq[g] = pex(t - 1)[64 * g];
