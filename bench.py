@@ -589,7 +589,8 @@ def main():
         t_s = ring_sim.time_device_rounds(qd, kd, vd, N, sra.STRIPED, reps=reps)
         critical = ring_sim.project(t_s, t_c, ring_sim.kv_block_bytes(B, S, H, D, N, q.element_size()))
         critical["note"] = ("one launch per (device, round) on this GPU; ring time = sum over rounds of "
-                            "max(slowest device, K/V transfer at the assumed link bandwidth)")
+                            "max(slowest device, K/V transfer at the assumed link bandwidth); prefetch time = "
+                            "every block sent at the start over the direct links, round r waiting for its block")
         critical["reps"] = reps
         note("simulated ring done")
 

@@ -18,6 +18,15 @@ with the round's compute (a stated model, not a measurement: the pages name
 no interconnect, and every simulated device runs on the same GPU). The projected speedup of
 striped over contiguous is the ratio of ring times at the same shape.
 
+A second model fits a node whose GPUs are all directly linked (an MI355X has 7
+links to the 7 other GPUs of its node): instead of passing blocks around the
+ring, every device sends its own block to all others at the start, one block
+per link at a time, so the block of round r arrives after ceil(r / links)
+transfers, and round r starts when both round r-1 has finished and its block
+is in:
+
+    prefetch time  = finish of the last round, round r on [max(end of r-1, ceil(r / links) t_comm), + max_d t(d, r)]
+
 Host-side functions (``critical_path``, ``ring_time``, ``kv_block_bytes``,
 ``project``) are plain Python; ``time_device_rounds`` needs the GPU library.
 """
@@ -27,6 +36,7 @@ import json
 import statistics
 
 DEFAULT_LINK_GBPS = 153.0   # assumed bandwidth of one device-to-device link, GB/s
+DEFAULT_LINKS = 7           # direct links per GPU in an 8-GPU MI355X node
 
 
 def critical_path(t):
@@ -39,6 +49,17 @@ def ring_time(t, t_comm):
     return float(sum(max(max(row), t_comm) for row in t))
 
 
+def prefetch_time(t, t_comm, links=DEFAULT_LINKS):
+    """Time of all rounds when every remote block is sent directly at the start
+    over `links` links (one block per link at a time): round r >= 1 waits for
+    its block, which arrives after ceil(r / links) transfers."""
+    end = 0.0
+    for r, row in enumerate(t):
+        arrive = -(-r // links) * t_comm if r > 0 else 0.0
+        end = max(end, arrive) + max(row)
+    return float(end)
+
+
 def mean_path(t):
     """sum over rounds of the mean device time: the time if work were perfectly balanced."""
     return float(sum(sum(row) / len(row) for row in t))
@@ -49,17 +70,19 @@ def kv_block_bytes(batch, seq, heads, head_dim, n_dev, elem_bytes=2):
     return 2 * batch * (seq // n_dev) * heads * head_dim * elem_bytes
 
 
-def project(t_striped, t_contig, block_bytes, link_gbps=DEFAULT_LINK_GBPS):
+def project(t_striped, t_contig, block_bytes, link_gbps=DEFAULT_LINK_GBPS, links=DEFAULT_LINKS):
     """Projected ring times and speedups from per-(round, device) times in ms."""
     t_comm = block_bytes / (link_gbps * 1e9) * 1e3
-    out = {"t_comm_ms": t_comm, "link_GBps": link_gbps, "kv_block_bytes": block_bytes}
+    out = {"t_comm_ms": t_comm, "link_GBps": link_gbps, "kv_block_bytes": block_bytes, "direct_links": links}
     for name, t in (("striped", t_striped), ("contiguous", t_contig)):
         out[name] = {"critical_path_ms": critical_path(t), "ring_ms": ring_time(t, t_comm),
+                     "prefetch_ms": prefetch_time(t, t_comm, links),
                      "balanced_ms": mean_path(t),
                      "round_max_ms": [max(row) for row in t],
                      "round_max_over_mean": [max(row) / (sum(row) / len(row)) for row in t]}
     out["speedup_compute_bound"] = out["contiguous"]["critical_path_ms"] / out["striped"]["critical_path_ms"]
     out["speedup_with_comm"] = out["contiguous"]["ring_ms"] / out["striped"]["ring_ms"]
+    out["speedup_with_prefetch"] = out["contiguous"]["prefetch_ms"] / out["striped"]["prefetch_ms"]
     return out
 
 
@@ -112,7 +135,7 @@ def time_device_rounds(q, k, v, n_dev, layout, reps=3):
     return [[statistics.median(samples[r][d]) for d in range(n_dev)] for r in range(n_dev)]
 
 
-def simulate(workload="long", reps=3, link_gbps=DEFAULT_LINK_GBPS, seed=None):
+def simulate(workload="long", reps=3, link_gbps=DEFAULT_LINK_GBPS, seed=None, links=DEFAULT_LINKS):
     """Times both layouts of a named workload and returns the projection."""
     import torch
     import striped_ring_attention_amd as sra
@@ -128,7 +151,7 @@ def simulate(workload="long", reps=3, link_gbps=DEFAULT_LINK_GBPS, seed=None):
     del q, k, v, x
     t_striped = time_device_rounds(qs, ks, vs, N, sra.STRIPED, reps)
     B, S, H, D = qs.shape
-    res = project(t_striped, t_contig, kv_block_bytes(B, S, H, D, N, qs.element_size()), link_gbps)
+    res = project(t_striped, t_contig, kv_block_bytes(B, S, H, D, N, qs.element_size()), link_gbps, links)
     pairs = {name: sra.count_live_pairs(S, N, lay).numpy() for name, lay in
              (("striped", sra.STRIPED), ("contiguous", sra.CONTIGUOUS))}
     ideal = {n: float(p.max(axis=1).sum()) for n, p in pairs.items()}
@@ -143,8 +166,9 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--link-gbps", type=float, default=DEFAULT_LINK_GBPS)
+    ap.add_argument("--links", type=int, default=DEFAULT_LINKS, help="direct links per GPU (prefetch model)")
     args = ap.parse_args()
-    print(json.dumps(simulate(args.workload, args.reps, args.link_gbps)), flush=True)
+    print(json.dumps(simulate(args.workload, args.reps, args.link_gbps, links=args.links)), flush=True)
 
 
 if __name__ == "__main__":
