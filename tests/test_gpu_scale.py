@@ -1,8 +1,8 @@
-"""GPU parity with an explicit softmax scale (the descriptor's scale field,
-instead of the default 1/sqrt(head_dim)): the ring forward on both schedules
-and layouts, the fp32 rounds, and the backward, against the oracle evaluated
-with the same scale. A kernel that ignored the field would fail here, since
-every other test runs at the default scale."""
+"""GPU parity on descriptor settings the other tests leave at one value:
+an explicit softmax scale (instead of the default 1/sqrt(head_dim)) for the
+ring forward on both schedules and layouts, the fp32 rounds and the backward,
+against the oracle evaluated with the same scale (a kernel that ignored the
+field would fail here); and 48 or 64 heads, i.e. token rows of 24 and 32 KiB."""
 
 import sys
 
@@ -63,3 +63,26 @@ def test_explicit_scale_fp32_rounds(sra):
         e_o, e_l = err(o, o_ref), err(lse, l_ref)
         say(f"fp32 layout {layout}: O {e_o:.3g} LSE {e_l:.3g}")
         assert e_o <= 1e-5 and e_l <= 1e-5
+
+
+@pytest.mark.parametrize("S,N,H", [(512, 4, 48), (256, 16, 64)])
+def test_many_heads_forward_and_backward(sra, S, N, H):
+    """Token rows of 24 and 32 KiB (48 and 64 heads): one head's consecutive
+    tokens are that far apart, and 16 of them in original order with N = 16.
+    Fused and per-round forwards and the backward against the dense oracle."""
+    g = torch.Generator().manual_seed(79 + H)
+    x = {n: (torch.randn((1, S, H, 128), generator=g) * 0.5).to(torch.bfloat16) for n in ("q", "k", "v")}
+    x["do"] = torch.randn((1, S, H, 128), generator=g).to(torch.bfloat16)
+    o_ref, l_ref = oracle.dense_causal_attention(x["q"], x["k"], x["v"])
+    ref = oracle.dense_causal_backward(x["q"], x["k"], x["v"], o_ref, l_ref, x["do"])
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    for schedule in (sra.SCHEDULE_PER_ROUND, sra.SCHEDULE_FUSED):
+        say("S", S, "N", N, "H", H, "schedule", schedule)
+        o, lse = sra.ring_attn_fwd(q, k, v, N, oracle.STRIPED, schedule=schedule, order=sra.ORDER_ORIGINAL)
+        torch.cuda.synchronize()
+        assert err(o, o_ref) <= 2e-2 and err(lse, l_ref) <= 2e-2
+    grads = sra.ring_attn_bwd(q, k, v, o, lse, do, N, oracle.STRIPED, order=sra.ORDER_ORIGINAL)
+    torch.cuda.synchronize()
+    errs = [err(gr, r) for gr, r in zip(grads, ref)]
+    say(f"  backward: dQ {errs[0]:.3g} dK {errs[1]:.3g} dV {errs[2]:.3g}")
+    assert max(errs) <= 2e-2
