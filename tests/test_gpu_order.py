@@ -75,7 +75,10 @@ def test_round_original_order_device_filter(sra):
         assert torch.equal(o1, sra.unstripe(o2, N)) and torch.equal(l1, sra.unstripe(l2, N))
 
 
-@pytest.mark.parametrize("S,H,N", [(8192, 4, 8), (8 * 300, 3, 8), (16, 1, 16)])
+# (32768, 32, 16) and (16000, 32, 16): the Very long ring's N and heads, so a
+# device's consecutive tokens are 128 KiB apart in original order (a dK/dV
+# query tile spans 4 MiB), with slabs a multiple of the tiles and ragged.
+@pytest.mark.parametrize("S,H,N", [(8192, 4, 8), (8 * 300, 3, 8), (16, 1, 16), (32768, 32, 16), (16000, 32, 16)])
 def test_bwd_original_order_bit_identical(sra, S, H, N):
     q, k, v, do = rand_bf16(S, H, 90 + S)
     for layout in (oracle.CONTIGUOUS, oracle.STRIPED):
